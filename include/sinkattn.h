@@ -1,0 +1,182 @@
+/*
+ * sinkattn.h -- C ABI of the MI355X (gfx950) sink-attention library.
+ *
+ * The operation is the attention layer of the MiMo-V2-Flash Technical Report
+ * (full translation, garden.houmin.site/digest/mimo-v2-flash):
+ *
+ *   Section 2.2, equations 1-4: for one head, a_ij = q_i . k_j / sqrt(d);
+ *   s_ij = exp(a_ij - m_i) / (exp(sink - m_i) + sum_j' exp(a_ij' - m_i)),
+ *   m_i = max(max_j a_ij, sink); o_i = sum_j s_ij v_j.  One learnable sink
+ *   logit per head sits in the denominator only (it has no value vector).
+ *
+ *   Section 2.1 and Table 1: grouped-query attention, sliding-window (W = 128,
+ *   64 query / 8 KV heads) or global (64 query / 4 KV heads) layers; QK head
+ *   dim 192, V head dim 128; RoPE only on the first 64 dims of q and k.
+ *
+ *   Section 2.3.1: decoding is memory-bound because every request keeps its
+ *   own KV cache; draft tokens are verified by the main model in one pass
+ *   without extra KV-cache traffic (the verify entry point below).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates or frees device memory and keeps no pointer after return.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued asynchronously; results are valid once the caller has
+ *    synchronised the stream.  Host-side argument errors are returned before
+ *    anything is enqueued; a device fault surfaces at the caller's sync.
+ *  - Every function returns 0 (SINKATTN_OK) or a negative SINKATTN_ERR_* code;
+ *    sinkattn_status_string() names it.
+ *  - dtype is SINKATTN_F32 or SINKATTN_BF16 and applies to q, k, v, o, the
+ *    caches and the new-token tensors alike.  `sink` is always fp32 [Hq] in
+ *    logit units (not divided by sqrt(d)); -INFINITY disables a head's sink.
+ *    `lse` (when requested) is always fp32.
+ *  - Layouts are dense row-major:
+ *        q [B,T,Hq,dqk]   k [B,T,Hkv,dqk]   v [B,T,Hkv,dv]   o [B,T,Hq,dv]
+ *        lse [B,Hq,T]
+ *        caches, head-major: k_cache [B,Hkv,cap,dqk], v_cache [B,Hkv,cap,dv]
+ *    Query head h reads KV head h / (Hq/Hkv).
+ *  - scale <= 0 selects 1/sqrt(dqk) (the report's d is the QK head dim).
+ *  - A sliding window of W holds W keys including the query itself: a key at
+ *    position p is visible to a query at position P iff P - W < p <= P.
+ *  - Supported in this version: dqk == 192, dv == 128 (SINKATTN_ERR_UNSUPPORTED
+ *    otherwise); Hq % Hkv == 0.  The bf16 paths need (Hq/Hkv) % 8 == 0.
+ *  - Calls on different streams that write the same buffers race; nothing else
+ *    is shared between calls.
+ */
+#ifndef SINKATTN_H
+#define SINKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SINKATTN_ABI_VERSION 1
+
+enum {
+    SINKATTN_OK = 0,
+    SINKATTN_ERR_NULL_PTR = -1,    /* a required pointer is NULL */
+    SINKATTN_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    SINKATTN_ERR_DTYPE = -3,       /* unknown dtype code */
+    SINKATTN_ERR_UNSUPPORTED = -4, /* valid but not implemented (head dims, group) */
+    SINKATTN_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+    SINKATTN_ERR_CAPACITY = -6,    /* cache capacity too small for the request */
+    SINKATTN_ERR_ALIAS = -7,       /* an output overlaps an input it must not */
+    SINKATTN_ERR_HIP = -8          /* the HIP runtime reported an error at launch */
+};
+
+enum { SINKATTN_F32 = 0, SINKATTN_BF16 = 1 };
+enum { SINKATTN_CACHE_RING = 0, SINKATTN_CACHE_CONTIG = 1 };
+enum { SINKATTN_ROPE_INTERLEAVED = 0, SINKATTN_ROPE_HALF = 1 };
+
+/* Version of this ABI (SINKATTN_ABI_VERSION of the built library). */
+int sinkattn_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *sinkattn_status_string(int status);
+
+/*
+ * Partial rotary position embedding, in place (Section 2.1: RoPE on the first
+ * 64 dims of q and k; RoFormer; bases from Section 3.2: 1e4 for SWA layers,
+ * 6.4e5 then 5e6 for global layers).
+ *   x    [n_tok, n_heads, head_dim] (dtype), rotated in place
+ *   pos  device int32 [n_tok]: absolute position of each token (>= 0)
+ *   rope_dim: even, <= head_dim; dims >= rope_dim are left bit-identical
+ *   style: SINKATTN_ROPE_INTERLEAVED pairs (2c, 2c+1);
+ *          SINKATTN_ROPE_HALF pairs (c, c + rope_dim/2)
+ *   angle = pos * base^(-2c/rope_dim) is formed in fp64; the rotation is done
+ *   in fp32 and rounded once to dtype (round to nearest even).
+ */
+int sinkattn_rope_partial(void *x, int dtype, int64_t n_tok, int n_heads, int head_dim,
+                          int rope_dim, const int32_t *pos, double base, int style,
+                          void *stream);
+
+/*
+ * Causal sliding-window prefill (Section 2.2; window from Table 1).
+ *   q, k, v, o as in the conventions, positions 0..T-1 in every sequence;
+ *   window >= 1 (W); lse may be NULL.  o must not overlap q, k or v.
+ */
+int sinkattn_prefill_swa(const void *q, const void *k, const void *v, const float *sink,
+                         void *o, float *lse, int B, int T, int Hq, int Hkv, int dqk, int dv,
+                         int window, float scale, int dtype, void *stream);
+
+/* Causal prefill over the full context (global-attention layers, Table 1). */
+int sinkattn_prefill_global(const void *q, const void *k, const void *v, const float *sink,
+                            void *o, float *lse, int B, int T, int Hq, int Hkv, int dqk,
+                            int dv, float scale, int dtype, void *stream);
+
+/*
+ * Bytes of fp32 workspace that sinkattn_decode / sinkattn_verify need for a
+ * split-K pass over a contiguous cache with at most `max_splits` splits:
+ * B * n_q * Hq * max_splits * (dv + 2) * 4.  Zero if max_splits <= 1.
+ */
+size_t sinkattn_decode_workspace_bytes(int B, int Hq, int dv, int n_q, int max_splits);
+
+/*
+ * One decode step (Section 2.3.1: one new token per sequence).
+ *   q      [B,Hq,dqk]   k_new [B,Hkv,dqk]   v_new [B,Hkv,dv]   o [B,Hq,dv]
+ *   cache_len: device int32 [B], the number of tokens already cached; the new
+ *          token sits at position P = cache_len[b].  Not modified.
+ *   kind = SINKATTN_CACHE_RING: a W-slot ring per (sequence, KV head); position
+ *          p lives in slot p % cap; requires window >= 1 and cap >= window.
+ *          The query sees positions max(0, P-W+1) .. P.
+ *   kind = SINKATTN_CACHE_CONTIG: position p lives at index p; requires
+ *          max_len_hint < cap.  window <= 0 is global (positions 0..P),
+ *          window >= 1 restricts to the last W positions.
+ *   The step also stores k_new/v_new into the cache at position P (ring slot
+ *   P % cap, or index P).  The attention itself reads the new token from
+ *   k_new/v_new, never from the cache, so that store does not race with it.
+ *   max_len_hint: host bound on max(cache_len); sizes the split grid.
+ *   num_splits: CONTIG only: 0 = choose automatically, 1 = no split, S > 1 = at
+ *          most S context chunks merged by an exact log-sum-exp combine that
+ *          adds the sink once.  RING ignores it (<= W+1 keys).
+ *   workspace / ws_bytes: fp32 scratch of sinkattn_decode_workspace_bytes(B,
+ *          Hq, dv, 1, S) bytes for the chosen S > 1 (may be NULL when no split
+ *          is taken; the automatic choice never exceeds what ws_bytes holds).
+ */
+int sinkattn_decode(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                    void *v_cache, int kind, int cap, const int32_t *cache_len,
+                    int max_len_hint, const float *sink, void *o, int B, int Hq, int Hkv,
+                    int dqk, int dv, int window, float scale, int num_splits,
+                    void *workspace, size_t ws_bytes, int dtype, void *stream);
+
+/*
+ * Multi-query speculative verification (Section 2.3.1 and Section 5: the main
+ * model scores 1 + K draft tokens in one pass; Table 10 uses 3 draft heads).
+ *   q [B,nq,Hq,dqk]; k_new/v_new [B,nq,Hkv,d]; o [B,nq,Hq,dv]; 1 <= nq <= 8.
+ *   Query t sits at position P + t (P = cache_len[b]) and sees the visible
+ *   cached positions plus new tokens 0..t.  THE CACHES ARE READ-ONLY: drafts
+ *   are taken from k_new/v_new and committed later with sinkattn_kv_append
+ *   (writing them into a W-slot ring first would overwrite keys still inside
+ *   query 0's window).  Other arguments as in sinkattn_decode.
+ *   Supported: nq * (Hq/Hkv) <= 64 on the bf16 path.
+ */
+int sinkattn_verify(const void *q, const void *k_new, const void *v_new,
+                    const void *k_cache, const void *v_cache, int kind, int cap,
+                    const int32_t *cache_len, int max_len_hint, const float *sink, void *o,
+                    int B, int nq, int Hq, int Hkv, int dqk, int dv, int window, float scale,
+                    int num_splits, void *workspace, size_t ws_bytes, int dtype,
+                    void *stream);
+
+/*
+ * Commit accepted tokens into a cache (the step after verification).
+ *   k_new [B,n,Hkv,dqk], v_new [B,n,Hkv,dv]: tokens at positions
+ *   cache_len[b] .. cache_len[b]+n-1.  n_accept: device int32 [B] (NULL = n):
+ *   only tokens t < min(n_accept[b], n) are written.  RING: position p goes to
+ *   slot p % cap, and when more than cap tokens are written only the last cap
+ *   of them are stored (so one call can lay a whole prefill into a ring).
+ *   CONTIG: index p; positions >= cap are dropped (callers size cap).
+ *   cache_len is not modified.
+ */
+int sinkattn_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                       int kind, int cap, const int32_t *cache_len, const int32_t *n_accept,
+                       int B, int n, int Hkv, int dqk, int dv, int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKATTN_H */
