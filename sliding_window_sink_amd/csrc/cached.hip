@@ -1,0 +1,430 @@
+// cached.hip -- decode / speculative-verify sink attention over a KV cache (gfx950, bf16).
+//
+// Queries at positions P + t (P = cache_len[b], t < nq) attend to the cached
+// keys of their window plus the new tokens 0..t (MiMo-V2-Flash Technical
+// Report, Section 2.2 for the sink softmax; Section 2.3.1 for decoding one
+// token, or verifying 1 + K draft tokens in one pass, over a per-request cache).
+//
+// Caches are head-major [B, Hkv, cap, d].  A sliding-window layer keeps a ring
+// of cap >= W slots (position p in slot p % cap); a global layer keeps a
+// contiguous cache (position p at index p).  Positions >= P are always read
+// from k_new / v_new, never from the cache: decode may therefore store its new
+// token into the cache in the same launch without racing the readers, and
+// verify never writes the cache at all.
+//
+// Decomposition: one workgroup (4 waves) per (sequence, KV group, context
+// chunk).  Columns of the 32x32 MFMA tile are (token, head) pairs of the KV
+// group: nq*group <= 64, so one or two column blocks.  The chunk's keys are cut
+// into blocks of 32 that the 4 waves take in turn; each wave keeps its own
+// online-softmax state (no sink), then the 4 states are merged through LDS.
+// With one chunk the merge adds the sink and writes o; with several it writes
+// the unnormalised (m, l, acc) of the chunk to the workspace and a combine
+// kernel adds the sink exactly once:
+//   M = max(sink, max_c m_c),  Z = e^(sink-M) + sum_c l_c e^(m_c-M),
+//   o = sum_c acc_c e^(m_c-M) / Z.
+//
+// Memory access: K and V are loaded straight from HBM into MFMA operand
+// registers (no LDS round trip; every byte is read once).  For K the lane that
+// owns A-row r reads 32 contiguous bytes of that key per k-step.  For V the
+// output-dim order is chosen as dim = 4*row + block, so each lane reads 8
+// contiguous bytes (4 dims) of 16 keys and two lanes cover a 256-byte row:
+// fully coalesced; a register shuffle then builds the V^T operands.
+#include "common.h"
+
+namespace sinkattn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kKb = 32;
+constexpr int kMergeStride = kDv + 4;  // floats per (wave, column): acc[128], m, l, pad
+
+struct CachedGeom {
+    int b, g, group, P, lo, hi, rlo, rhi;
+};
+
+__device__ __forceinline__ CachedGeom cached_geom(const CachedArgs &a, int split, int bg) {
+    CachedGeom c;
+    c.g = bg % a.Hkv;
+    c.b = bg / a.Hkv;
+    c.group = a.Hq / a.Hkv;
+    c.P = clamp_len(a.cache_len[c.b], a.max_len);
+    c.lo = a.window > 0 ? max(0, c.P - a.window + 1) : 0;
+    c.hi = c.P + a.nq;
+    c.rlo = c.lo;
+    c.rhi = c.hi;
+    if (a.n_splits > 1) {
+        c.rlo = max(c.lo, split * a.chunk);
+        c.rhi = min(c.hi, (split + 1) * a.chunk);
+    }
+    return c;
+}
+
+// Row of key position p in the cache or in the new-token tensor (nullptr if p is
+// outside [rlo, rhi)).
+__device__ __forceinline__ const uint16_t *key_row(const CachedArgs &a, const CachedGeom &c, int p,
+                                                   const uint16_t *cache, const uint16_t *fresh,
+                                                   int d) {
+    if (p < c.rlo || p >= c.rhi)
+        return nullptr;
+    if (p < c.P) {
+        const int slot = a.ring ? (p % a.cap) : p;
+        return cache + (((size_t)c.b * a.Hkv + c.g) * a.cap + slot) * d;
+    }
+    return fresh + (((size_t)c.b * a.nq + (p - c.P)) * a.Hkv + c.g) * d;
+}
+
+template <int NCB>
+__global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) float merge[kWaves - 1][32][kMergeStride];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 31, hh = lane >> 5;
+    const int split = blockIdx.x % a.n_splits;
+    const CachedGeom c = cached_geom(a, split, blockIdx.x / a.n_splits);
+    const int group = c.group;
+    const int n_cols = a.nq * group;
+
+    const uint16_t *kc = (const uint16_t *)a.k_cache;
+    const uint16_t *vc = (const uint16_t *)a.v_cache;
+    const uint16_t *kn = (const uint16_t *)a.k_new;
+    const uint16_t *vn = (const uint16_t *)a.v_new;
+
+    // Decode: store the new token into the cache (slot / index P).  Nothing in
+    // this launch reads that cache row.
+    if (a.write_new && split == 0) {
+        const int slot = a.ring ? (c.P % a.cap) : c.P;
+        if (a.ring || c.P < a.cap) {
+            uint16_t *kd = (uint16_t *)a.k_cache + (((size_t)c.b * a.Hkv + c.g) * a.cap + slot) * kDqk;
+            uint16_t *vd = (uint16_t *)a.v_cache + (((size_t)c.b * a.Hkv + c.g) * a.cap + slot) * kDv;
+            const uint16_t *ks = kn + ((size_t)c.b * a.nq * a.Hkv + c.g) * kDqk;
+            const uint16_t *vs = vn + ((size_t)c.b * a.nq * a.Hkv + c.g) * kDv;
+            if (tid < kDqk / 8)
+                *(uint4 *)(kd + tid * 8) = *(const uint4 *)(ks + tid * 8);
+            else if (tid < kDqk / 8 + kDv / 8)
+                *(uint4 *)(vd + (tid - kDqk / 8) * 8) = *(const uint4 *)(vs + (tid - kDqk / 8) * 8);
+        }
+    }
+
+    // Q^T operands; column cb*32 + r is (token t, head) = divmod(column, group).
+    bf16x8 qf[NCB][kDqk / 16];
+    int qpos[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int col = cb * 32 + r;
+        const bool ok = col < n_cols;
+        const int t = ok ? col / group : 0;
+        const int h = c.g * group + (ok ? col % group : 0);
+        qpos[cb] = ok ? c.P + t : -1;
+        const uint16_t *qrow = (const uint16_t *)a.q + (((size_t)c.b * a.nq + t) * a.Hq + h) * kDqk;
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s) {
+            uint4 u = ok ? *(const uint4 *)(qrow + (2 * s + hh) * 8) : make_uint4(0, 0, 0, 0);
+            qf[cb][s] = as_bf16x8(u);
+        }
+    }
+
+    float m[NCB], l[NCB];
+    f32x16 acc[NCB][4];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        m[cb] = -INFINITY;
+        l[cb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            acc[cb][db] = f32x16{};
+    }
+
+    const int nkeys = max(0, c.rhi - c.rlo);
+    const int nblk = (nkeys + kKb - 1) / kKb;
+    const int window = a.window;
+
+    for (int j = wave; j < nblk; j += kWaves) {
+        const int kb = c.rlo + j * kKb;
+        // K: A-row r holds key key_of_row(r); k-step s reads dims (2s+hh)*8 .. +7.
+        uint4 kf[kDqk / 16];
+        {
+            const uint16_t *row = key_row(a, c, kb + key_of_row(r), kc, kn, kDqk);
+#pragma unroll
+            for (int s = 0; s < kDqk / 16; ++s)
+                kf[s] = row ? *(const uint4 *)(row + (2 * s + hh) * 8) : make_uint4(0, 0, 0, 0);
+        }
+        // V: keys 16*hh + i (i < 16), dims 4r .. 4r+3.
+        uint2 vf[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint16_t *row = key_row(a, c, kb + 16 * hh + i, vc, vn, kDv);
+            vf[i] = row ? *(const uint2 *)(row + 4 * r) : make_uint2(0, 0);
+        }
+
+        f32x16 sc[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+            sc[cb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                sc[cb] = mfma32x32x16(as_bf16x8(kf[s]), qf[cb][s], sc[cb]);
+
+        // V^T operands: block db (dims 4*row + db), k-step t (keys 16hh + 8t + e).
+        bf16x8 va[4][2];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const uint2 lo = vf[8 * t + 2 * e2], hi = vf[8 * t + 2 * e2 + 1];
+                    const uint32_t wl = (db < 2) ? lo.x : lo.y;
+                    const uint32_t wh = (db < 2) ? hi.x : hi.y;
+                    const uint32_t a16 = (db & 1) ? (wl >> 16) : (wl & 0xffffu);
+                    const uint32_t b16 = (db & 1) ? (wh >> 16) : (wh & 0xffffu);
+                    w[e2] = a16 | (b16 << 16);
+                }
+                va[db][t] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+            }
+
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            float x[16];
+            float bm = -INFINITY;
+            const int qp = qpos[cb];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int p = kb + 16 * hh + i;
+                const bool vis = p < c.rhi && p <= qp && (window <= 0 || qp - p < window);
+                x[i] = vis ? sc[cb][i] * scale_log2 : -INFINITY;
+                bm = fmaxf(bm, x[i]);
+            }
+            bm = max_across_halves(bm);
+            const float mn = fmaxf(m[cb], bm);
+            const float mu = (mn == -INFINITY) ? 0.f : mn;
+            const float alpha = fast_exp2(m[cb] - mu);
+            float ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                x[i] = fast_exp2(x[i] - mu);
+                ps += x[i];
+            }
+            l[cb] = l[cb] * alpha + ps;
+            m[cb] = mn;
+            bf16x8 pb[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pb[t][e] = (__bf16)x[8 * t + e];
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                acc[cb][db] *= alpha;
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    acc[cb][db] = mfma32x32x16(va[db][t], pb[t], acc[cb][db]);
+            }
+        }
+    }
+
+    // Merge the 4 waves' states, one column block at a time: waves 1..3 park
+    // (acc, m, l) in LDS, wave 0 folds them into its registers and writes.
+    const bool write_final = a.n_splits == 1;
+    const size_t rows_total = (size_t)a.B * a.nq * a.Hq;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int ncol = min(32, n_cols - cb * 32);
+        if (ncol <= 0)
+            break;
+        const float lt = sum_across_halves(l[cb]);
+        if (wave > 0 && r < ncol) {
+            float *e = &merge[wave - 1][r][0];
+            if (hh == 0) {
+                e[kDv] = m[cb];
+                e[kDv + 1] = lt;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float4 v4 = make_float4(acc[cb][0][i], acc[cb][1][i], acc[cb][2][i],
+                                              acc[cb][3][i]);
+                *(float4 *)&e[4 * c_row(i, hh)] = v4;
+            }
+        }
+        __syncthreads();
+        if (wave == 0 && r < ncol) {
+            const int col = cb * 32 + r;
+            const int t = col / group;
+            const int h = c.g * group + col % group;
+            const size_t row = ((size_t)c.b * a.nq + t) * a.Hq + h;
+            float mx = m[cb];
+#pragma unroll
+            for (int w = 0; w < kWaves - 1; ++w)
+                mx = fmaxf(mx, merge[w][r][kDv]);
+            float M = mx, zs = 0.f;
+            if (write_final) {
+                const float sink2 = a.sink[h] * kLog2e;
+                M = fmaxf(mx, sink2);
+                zs = (sink2 == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(sink2 - M);
+            }
+            const float f0 = (m[cb] == -INFINITY) ? 0.f : fast_exp2(m[cb] - M);
+            float fw[kWaves - 1];
+            float z = zs + lt * f0;
+#pragma unroll
+            for (int w = 0; w < kWaves - 1; ++w) {
+                const float mw = merge[w][r][kDv];
+                fw[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+                z += merge[w][r][kDv + 1] * fw[w];
+            }
+            const float scale_out = write_final ? (z > 0.f ? 1.f / z : 0.f) : 1.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int d0 = 4 * c_row(i, hh);  // dims d0 .. d0+3 (blocks 0..3)
+                float vals[4];
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    vals[db] = acc[cb][db][i] * f0;
+#pragma unroll
+                for (int w = 0; w < kWaves - 1; ++w) {
+                    const float4 p4 = *(const float4 *)&merge[w][r][d0];
+                    vals[0] += p4.x * fw[w];
+                    vals[1] += p4.y * fw[w];
+                    vals[2] += p4.z * fw[w];
+                    vals[3] += p4.w * fw[w];
+                }
+                if (write_final) {
+                    uint2 u;
+                    u.x = pack_bf16x2(vals[0] * scale_out, vals[1] * scale_out);
+                    u.y = pack_bf16x2(vals[2] * scale_out, vals[3] * scale_out);
+                    *(uint2 *)((uint16_t *)a.o + row * kDv + d0) = u;
+                } else {
+                    const size_t slot = row * a.n_splits + split;
+                    *(float4 *)&a.ws[2 * rows_total * a.n_splits + slot * kDv + d0] =
+                        make_float4(vals[0], vals[1], vals[2], vals[3]);
+                }
+            }
+            if (!write_final && hh == 0) {
+                const size_t slot = row * a.n_splits + split;
+                a.ws[slot] = M;
+                a.ws[rows_total * a.n_splits + slot] = (M == -INFINITY) ? 0.f : z;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Split-K combine: one wave per (b, t, h) row; adds the sink exactly once.
+__global__ __launch_bounds__(64) void combine_kernel(CachedArgs a, int out_bf16) {
+    const int row = blockIdx.x;  // ((b * nq) + t) * Hq + h
+    const int lane = threadIdx.x;
+    const int h = row % a.Hq;
+    const int b = row / (a.nq * a.Hq);
+    const int S = a.n_splits;
+    const size_t rows_total = (size_t)a.B * a.nq * a.Hq;
+    const float *wm = a.ws + (size_t)row * S;
+    const float *wl = a.ws + rows_total * S + (size_t)row * S;
+    const float *wa = a.ws + 2 * rows_total * S + (size_t)row * S * kDv;
+    const int P = clamp_len(a.cache_len[b], a.max_len);
+    const int lo = a.window > 0 ? max(0, P - a.window + 1) : 0;
+    const int hi = P + a.nq;
+    const int s0 = lo / a.chunk;
+    const int s1 = min(S, (hi + a.chunk - 1) / a.chunk);
+
+    const float sink2 = a.sink[h] * kLog2e;
+    float mx = sink2;
+    for (int s = s0 + lane; s < s1; s += 64)
+        mx = fmaxf(mx, wm[s]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float z = 0.f, acc0 = 0.f, acc1 = 0.f;
+    if (mx != -INFINITY) {
+        z = (sink2 == -INFINITY) ? 0.f : fast_exp2(sink2 - mx);
+        for (int s = s0; s < s1; ++s) {
+            const float ms = wm[s];
+            const float f = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mx);
+            z += wl[s] * f;
+            acc0 += wa[(size_t)s * kDv + lane] * f;
+            acc1 += wa[(size_t)s * kDv + 64 + lane] * f;
+        }
+    }
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    if (out_bf16) {
+        uint16_t *o = (uint16_t *)a.o + (size_t)row * kDv;
+        o[lane] = f32_to_bf16_bits(acc0 * inv);
+        o[64 + lane] = f32_to_bf16_bits(acc1 * inv);
+    } else {
+        float *o = (float *)a.o + (size_t)row * kDv;
+        o[lane] = acc0 * inv;
+        o[64 + lane] = acc1 * inv;
+    }
+}
+
+// Commit accepted tokens: one thread per 16-byte piece of a K or V row.
+__global__ void append_kernel(AppendArgs a, int row_bytes_k, int row_bytes_v) {
+    const int pk = row_bytes_k / 16, pv = row_bytes_v / 16;
+    const int per_tok = (pk + pv) * a.Hkv;
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)a.B * a.n * per_tok;
+    if (idx >= total)
+        return;
+    const int b = (int)(idx / ((size_t)a.n * per_tok));
+    const int rem = (int)(idx % ((size_t)a.n * per_tok));
+    const int t = rem / per_tok;
+    const int rr = rem % per_tok;
+    const int g = rr / (pk + pv);
+    const int piece = rr % (pk + pv);
+    const int nacc = a.n_accept ? min(a.n, max(0, a.n_accept[b])) : a.n;
+    if (t >= nacc)
+        return;
+    const int p = max(0, a.cache_len[b]) + t;
+    int slot;
+    if (a.ring) {
+        if (t < nacc - a.cap)  // a later token of this call takes the same slot
+            return;
+        slot = p % a.cap;
+    } else {
+        if (p >= a.cap)
+            return;
+        slot = p;
+    }
+    const size_t crow = ((size_t)b * a.Hkv + g) * a.cap + slot;
+    const size_t nrow = ((size_t)b * a.n + t) * a.Hkv + g;
+    if (piece < pk) {
+        const char *src = (const char *)a.k_new + nrow * row_bytes_k + piece * 16;
+        char *dst = (char *)a.k_cache + crow * row_bytes_k + piece * 16;
+        *(uint4 *)dst = *(const uint4 *)src;
+    } else {
+        const int pc = piece - pk;
+        const char *src = (const char *)a.v_new + nrow * row_bytes_v + pc * 16;
+        char *dst = (char *)a.v_cache + crow * row_bytes_v + pc * 16;
+        *(uint4 *)dst = *(const uint4 *)src;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s) {
+    const int n_cols = a.nq * (a.Hq / a.Hkv);
+    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    const dim3 grid((unsigned)(a.B * a.Hkv * a.n_splits)), block(kThreads);
+    if (n_cols <= 32)
+        cached_bf16_kernel<1><<<grid, block, 0, s>>>(a, scale_log2);
+    else
+        cached_bf16_kernel<2><<<grid, block, 0, s>>>(a, scale_log2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.n_splits == 1)
+        return e;
+    combine_kernel<<<dim3((unsigned)(a.B * a.nq * a.Hq)), dim3(64), 0, s>>>(a, 1);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs &a, int bf16, hipStream_t s) {
+    const int esz = bf16 ? 2 : 4;
+    const int rbk = kDqk * esz, rbv = kDv * esz;
+    const size_t total = (size_t)a.B * a.n * a.Hkv * ((rbk + rbv) / 16);
+    if (total == 0)
+        return hipSuccess;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    append_kernel<<<dim3(blocks), dim3(256), 0, s>>>(a, rbk, rbv);
+    return hipGetLastError();
+}
+
+}  // namespace sinkattn

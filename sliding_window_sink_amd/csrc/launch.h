@@ -1,0 +1,59 @@
+// launch.h -- internal parameter blocks and launchers (host <-> kernels).
+// Nothing here crosses the public C ABI; the host entry points in api.cpp
+// validate arguments and then call these launchers on the caller's stream.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sinkattn {
+
+// Causal prefill over positions 0..T-1 of B sequences (window <= 0: global).
+struct PrefillArgs {
+    const void *q, *k, *v;  // [B,T,Hq,192], [B,T,Hkv,192], [B,T,Hkv,128]
+    const float *sink;      // [Hq]
+    void *o;                // [B,T,Hq,128]
+    float *lse;             // [B,Hq,T] or nullptr
+    int B, T, Hq, Hkv, window;
+    float scale;            // softmax scale (natural units)
+};
+
+// Queries at positions cache_len[b] + t (t < nq) over a ring or contiguous
+// cache plus nq new tokens.
+struct CachedArgs {
+    const void *q;              // [B,nq,Hq,192]
+    const void *k_new, *v_new;  // [B,nq,Hkv,192], [B,nq,Hkv,128]
+    void *k_cache, *v_cache;    // [B,Hkv,cap,192], [B,Hkv,cap,128]
+    const int32_t *cache_len;   // [B] device
+    const float *sink;          // [Hq]
+    void *o;                    // [B,nq,Hq,128]
+    float *ws;                  // split workspace (fp32) or nullptr
+    int B, nq, Hq, Hkv, cap, window, ring, write_new;
+    int max_len;                // cache_len values are clamped to [0, max_len]
+    int n_splits, chunk;        // context chunks (chunk keys each) when n_splits > 1
+    float scale;
+};
+
+struct AppendArgs {
+    const void *k_new, *v_new;  // [B,n,Hkv,192], [B,n,Hkv,128]
+    void *k_cache, *v_cache;
+    const int32_t *cache_len, *n_accept;
+    int B, n, Hkv, cap, ring;
+};
+
+// Clamp a device-side cached length into the range the host validated.
+__device__ __forceinline__ int clamp_len(int len, int max_len) {
+    return len < 0 ? 0 : (len > max_len ? max_len : len);
+}
+
+hipError_t launch_rope(void *x, int bf16, int64_t n_tok, int n_heads, int head_dim, int rope_dim,
+                       const int32_t *pos, double base, int style, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s);
+hipError_t launch_cached_f32(const CachedArgs &a, hipStream_t s);
+hipError_t launch_append(const AppendArgs &a, int bf16, hipStream_t s);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace sinkattn

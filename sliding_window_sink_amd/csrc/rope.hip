@@ -1,0 +1,82 @@
+// rope.hip -- partial rotary position embedding, in place (gfx950).
+//
+// MiMo-V2-Flash Technical Report, Section 2.1: RoPE is applied only to the
+// first 64 of the 192 query/key dims; Section 3.2 gives the bases (1e4 for SWA
+// layers; 6.4e5, later 5e6, for global layers).  Pair c (c < rope_dim/2) is
+// rotated by angle pos * base^(-2c/rope_dim) (RoFormer).
+//
+// The angle is formed in fp64: in fp32, pos * theta loses ~1e-3 of a radian
+// near position 1e5, which is visible at fp32 tolerance.  Each workgroup
+// handles kTokens tokens: it first evaluates cos/sin once per (token, pair) in
+// fp64 into LDS, then every (token, head, pair) rotation reads them, so the
+// fp64 work does not scale with the head count.  Dims >= rope_dim are never
+// touched.  Traffic is one read and one write of the rotated dims.
+#include "common.h"
+
+namespace sinkattn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTokens = 8;
+constexpr int kMaxPairs = 128;  // rope_dim <= 256
+
+template <typename T>
+__device__ __forceinline__ float load_f(const T *p);
+template <>
+__device__ __forceinline__ float load_f<float>(const float *p) { return *p; }
+template <>
+__device__ __forceinline__ float load_f<uint16_t>(const uint16_t *p) { return bf16_bits_to_f32(*p); }
+
+__device__ __forceinline__ void store_f(float *p, float v) { *p = v; }
+__device__ __forceinline__ void store_f(uint16_t *p, float v) { *p = f32_to_bf16_bits(v); }
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rope_kernel(T *x, int64_t n_tok, int n_heads,
+                                                        int head_dim, int rope_dim,
+                                                        const int32_t *pos, double base, int style) {
+    __shared__ float cs[kTokens][kMaxPairs][2];
+    const int half = rope_dim / 2;
+    const int64_t tok0 = (int64_t)blockIdx.x * kTokens;
+    const int ntok = (int)min<int64_t>(kTokens, n_tok - tok0);
+    for (int idx = threadIdx.x; idx < ntok * half; idx += kThreads) {
+        const int tt = idx / half, c = idx % half;
+        const double theta = pow(base, -2.0 * (double)c / (double)rope_dim);
+        const double phi = (double)pos[tok0 + tt] * theta;
+        double sn, cn;
+        sincos(phi, &sn, &cn);
+        cs[tt][c][0] = (float)cn;
+        cs[tt][c][1] = (float)sn;
+    }
+    __syncthreads();
+    const int per_tok = n_heads * half;
+    for (int idx = threadIdx.x; idx < ntok * per_tok; idx += kThreads) {
+        const int tt = idx / per_tok;
+        const int rem = idx % per_tok;
+        const int h = rem / half, c = rem % half;
+        T *row = x + ((tok0 + tt) * n_heads + h) * (int64_t)head_dim;
+        const int i0 = style == 0 ? 2 * c : c;
+        const int i1 = style == 0 ? 2 * c + 1 : c + half;
+        const float x0 = load_f(row + i0), x1 = load_f(row + i1);
+        const float cn = cs[tt][c][0], sn = cs[tt][c][1];
+        store_f(row + i0, x0 * cn - x1 * sn);
+        store_f(row + i1, x0 * sn + x1 * cn);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rope(void *x, int bf16, int64_t n_tok, int n_heads, int head_dim, int rope_dim,
+                       const int32_t *pos, double base, int style, hipStream_t s) {
+    if (n_tok == 0 || n_heads == 0 || rope_dim == 0)
+        return hipSuccess;
+    const unsigned blocks = (unsigned)((n_tok + kTokens - 1) / kTokens);
+    if (bf16)
+        rope_kernel<uint16_t><<<dim3(blocks), dim3(kThreads), 0, s>>>(
+            (uint16_t *)x, n_tok, n_heads, head_dim, rope_dim, pos, base, style);
+    else
+        rope_kernel<float><<<dim3(blocks), dim3(kThreads), 0, s>>>(
+            (float *)x, n_tok, n_heads, head_dim, rope_dim, pos, base, style);
+    return hipGetLastError();
+}
+
+}  // namespace sinkattn

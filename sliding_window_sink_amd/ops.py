@@ -1,0 +1,241 @@
+"""ctypes binding of libsinkattn.so (include/sinkattn.h): argument marshalling only.
+
+Every function here checks tensor devices, dtypes, shapes and contiguity,
+allocates outputs with torch when the caller passes none, and calls the C entry
+point of the same name on torch's current stream.  All arithmetic runs in the
+HIP kernels.  There is no fallback: if the shared library is missing the first
+call raises ``SinkAttnUnavailable``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("SINKATTN_LIB", os.path.join(_HERE, "libsinkattn.so"))
+
+F32, BF16 = 0, 1
+RING, CONTIG = 0, 1
+INTERLEAVED, HALF = 0, 1
+DQK, DV = 192, 128
+
+_ERRORS = {-1: "NULL_PTR", -2: "SHAPE", -3: "DTYPE", -4: "UNSUPPORTED", -5: "WORKSPACE",
+           -6: "CAPACITY", -7: "ALIAS", -8: "HIP"}
+
+
+class SinkAttnUnavailable(RuntimeError):
+    pass
+
+
+class SinkAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("sinkattn error %d (%s): %s" % (code, _ERRORS.get(code, "?"), msg))
+        self.code = code
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def _bind(lib):
+    p, i32, i64, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_double, ctypes.c_size_t)
+    sig = {
+        "sinkattn_abi_version": ([], i32),
+        "sinkattn_status_string": ([i32], ctypes.c_char_p),
+        "sinkattn_rope_partial": ([p, i32, i64, i32, i32, i32, p, f64, i32, p], i32),
+        "sinkattn_prefill_swa": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, i32, p],
+                                 i32),
+        "sinkattn_prefill_global": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p],
+                                    i32),
+        "sinkattn_decode_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
+        "sinkattn_decode": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32, i32,
+                             f32, i32, p, sz, i32, p], i32),
+        "sinkattn_verify": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32, i32,
+                             i32, f32, i32, p, sz, i32, p], i32),
+        "sinkattn_kv_append": ([p, p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, i32, p], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+def lib():
+    """The loaded C library (raises SinkAttnUnavailable if it was not built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise SinkAttnUnavailable(
+                        "libsinkattn.so not found at %s; build it with "
+                        "`python -m sliding_window_sink_amd.build`" % LIB_PATH)
+                _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+EXPORTED = ["sinkattn_abi_version", "sinkattn_status_string", "sinkattn_rope_partial",
+            "sinkattn_prefill_swa", "sinkattn_prefill_global", "sinkattn_decode_workspace_bytes",
+            "sinkattn_decode", "sinkattn_verify", "sinkattn_kv_append"]
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise SinkAttnError(rc, lib().sinkattn_status_string(rc).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise SinkAttnError(-3, "tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise SinkAttnError(-1, "every tensor must live on the GPU")
+        if not t.is_contiguous():
+            raise SinkAttnError(-2, "every tensor must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _scale(scale):
+    return 0.0 if scale is None else float(scale)
+
+
+def abi_version() -> int:
+    return int(lib().sinkattn_abi_version())
+
+
+def rope_partial(x: torch.Tensor, pos: torch.Tensor, base: float, rope_dim: int = 64,
+                 style: int = INTERLEAVED) -> torch.Tensor:
+    """Partial RoPE in place on x [..., n_heads, head_dim]; pos int32 [n_tok]."""
+    _dev(x, pos)
+    if pos.dtype != torch.int32:
+        raise SinkAttnError(-3, "pos must be int32")
+    n_heads, head_dim = x.shape[-2], x.shape[-1]
+    n_tok = x.numel() // max(1, n_heads * head_dim)
+    if pos.numel() != n_tok:
+        raise SinkAttnError(-2, "pos must hold one position per token")
+    _check(lib().sinkattn_rope_partial(_ptr(x), _dtype_code(x), n_tok, n_heads, head_dim, rope_dim,
+                                       _ptr(pos), float(base), int(style), _stream()))
+    return x
+
+
+def _prefill(fn_name, q, k, v, sink, window, scale, out, return_lse):
+    _dev(q, k, v, sink, out)
+    B, T, Hq, dqk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    if k.shape != (B, T, Hkv, dqk) or v.shape[:3] != (B, T, Hkv) or sink.shape != (Hq,):
+        raise SinkAttnError(-2, "q/k/v/sink shapes disagree")
+    if sink.dtype != torch.float32 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise SinkAttnError(-3, "q, k, v share one dtype; sink is float32")
+    o = out if out is not None else torch.empty((B, T, Hq, dv), dtype=q.dtype, device=q.device)
+    if o.shape != (B, T, Hq, dv) or o.dtype != q.dtype:
+        raise SinkAttnError(-2, "bad output tensor")
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o), _ptr(lse), B, T, Hq, Hkv, dqk, dv]
+    if fn_name == "sinkattn_prefill_swa":
+        args.append(int(window))
+    args += [_scale(scale), _dtype_code(q), _stream()]
+    _check(getattr(lib(), fn_name)(*args))
+    return (o, lse) if return_lse else o
+
+
+def prefill_swa(q, k, v, sink, window: int = 128, scale=None, out=None, return_lse=False):
+    """Causal sliding-window prefill: q [B,T,Hq,192], k [B,T,Hkv,192], v [B,T,Hkv,128]."""
+    return _prefill("sinkattn_prefill_swa", q, k, v, sink, window, scale, out, return_lse)
+
+
+def prefill_global(q, k, v, sink, scale=None, out=None, return_lse=False):
+    """Causal full-context prefill (global-attention layer)."""
+    return _prefill("sinkattn_prefill_global", q, k, v, sink, 0, scale, out, return_lse)
+
+
+def decode_workspace_bytes(B: int, Hq: int, n_q: int = 1, max_splits: int = 64, dv: int = DV) -> int:
+    return int(lib().sinkattn_decode_workspace_bytes(B, Hq, dv, n_q, max_splits))
+
+
+def _cached(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window, max_len_hint,
+            num_splits, workspace, scale, out, verify):
+    _dev(q, k_new, v_new, k_cache, v_cache, cache_len, sink, workspace, out)
+    if cache_len.dtype != torch.int32:
+        raise SinkAttnError(-3, "cache_len must be int32")
+    if verify:
+        B, nq, Hq, dqk = q.shape
+    else:
+        B, Hq, dqk = q.shape
+        nq = 1
+    Bc, Hkv, cap, dk = k_cache.shape
+    dv = v_cache.shape[3]
+    if Bc != B or dk != dqk or v_cache.shape[:3] != (B, Hkv, cap) or sink.shape != (Hq,):
+        raise SinkAttnError(-2, "cache / query shapes disagree")
+    want_new = (B, nq, Hkv) if verify else (B, Hkv)
+    if tuple(k_new.shape[:-1]) != want_new or tuple(v_new.shape[:-1]) != want_new:
+        raise SinkAttnError(-2, "k_new/v_new shapes disagree")
+    oshape = (B, nq, Hq, dv) if verify else (B, Hq, dv)
+    o = out if out is not None else torch.empty(oshape, dtype=q.dtype, device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    args = [_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), int(kind), cap,
+            _ptr(cache_len), int(max_len_hint), _ptr(sink), _ptr(o), B]
+    if verify:
+        args.append(nq)
+    args += [Hq, Hkv, dqk, dv, int(window), _scale(scale), int(num_splits), ws_ptr, ws_bytes,
+             _dtype_code(q), _stream()]
+    fn = lib().sinkattn_verify if verify else lib().sinkattn_decode
+    _check(fn(*args))
+    return o
+
+
+def decode(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind=RING, window=128,
+           max_len_hint=None, num_splits=0, workspace=None, scale=None, out=None):
+    """One decode step; also stores k_new/v_new into the cache at cache_len."""
+    if max_len_hint is None:
+        raise SinkAttnError(-2, "max_len_hint (host bound on cache_len) is required")
+    return _cached(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window, max_len_hint,
+                   num_splits, workspace, scale, out, verify=False)
+
+
+def verify(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind=RING, window=128,
+           max_len_hint=None, num_splits=0, workspace=None, scale=None, out=None):
+    """Multi-query verification; the caches are read-only."""
+    if max_len_hint is None:
+        raise SinkAttnError(-2, "max_len_hint (host bound on cache_len) is required")
+    return _cached(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window, max_len_hint,
+                   num_splits, workspace, scale, out, verify=True)
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, cache_len, kind=RING, n_accept=None):
+    """Store tokens k_new/v_new [B,n,Hkv,d] at positions cache_len[b] + t."""
+    _dev(k_new, v_new, k_cache, v_cache, cache_len, n_accept)
+    B, n, Hkv, dqk = k_new.shape
+    cap = k_cache.shape[2]
+    dv = v_new.shape[3]
+    if k_cache.dtype != k_new.dtype or v_cache.dtype != k_new.dtype or v_new.dtype != k_new.dtype:
+        raise SinkAttnError(-3, "caches and new tokens share one dtype")
+    _check(lib().sinkattn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                    int(kind), cap, _ptr(cache_len), _ptr(n_accept), B, n, Hkv,
+                                    dqk, dv, _dtype_code(k_new), _stream()))
+
+
+def default_scale(dqk: int = DQK) -> float:
+    return 1.0 / math.sqrt(dqk)

@@ -1,0 +1,40 @@
+"""Shared helpers of the GPU parity tests (tolerances, conversions)."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+# Tolerances stated for the hot path: fp32 inputs max|d| <= 1e-4; bf16 inputs
+# with fp32 accumulation |d| <= 2e-2 + 1e-2 |oracle| elementwise.
+F32_ATOL = 1e-4
+BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def assert_close(got: torch.Tensor, ref: np.ndarray, dtype, what: str = ""):
+    g = to64(got)
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), what + ": non-finite output"
+    err = np.abs(g - ref)
+    if dtype == torch.float32:
+        worst = float(err.max()) if err.size else 0.0
+        assert worst <= F32_ATOL, "%s: max|d| = %.3g > %.1g" % (what, worst, F32_ATOL)
+    else:
+        bound = BF16_ATOL + BF16_RTOL * np.abs(ref)
+        bad = err > bound
+        if bad.any():
+            idx = np.unravel_index(np.argmax(err - bound), err.shape)
+            raise AssertionError("%s: %d elements out of tolerance, worst at %s: got %.5g ref %.5g"
+                                 % (what, int(bad.sum()), idx, g[idx], ref[idx]))
+    return float(err.max()) if err.size else 0.0
+
+
+def sink_for_half_mass(n_keys: int) -> float:
+    """A sink logit that takes about half of the softmax mass when the n_keys
+    logits are q.k/sqrt(192) with q, k ~ N(0,1) (logits ~ N(0,1): E e^a = e^0.5)."""
+    return math.log(max(1, n_keys)) + 0.5

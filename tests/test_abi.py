@@ -1,0 +1,136 @@
+"""The C-ABI library loads on the CPU, exports what include/sinkattn.h declares,
+and rejects bad arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sliding_window_sink_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkattn.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, CAP, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+P = ctypes.c_void_p
+FAKE = [P((i + 1) << 36) for i in range(12)]  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        pytest.fail("libsinkattn.so is not built (python -m sliding_window_sink_amd.build)")
+    return ops.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(sinkattn_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(ops.EXPORTED) == names
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sinkattn_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        s = lib.sinkattn_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.sinkattn_status_string(12345) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.sinkattn_decode_workspace_bytes(32, 64, 128, 1, 65) == 32 * 64 * 65 * 130 * 4
+    assert lib.sinkattn_decode_workspace_bytes(4, 8, 128, 4, 1) == 0
+
+
+def prefill(lib, *, q=FAKE[0], k=FAKE[1], v=FAKE[2], sink=FAKE[3], o=FAKE[4], lse=None, B=1,
+            T=64, Hq=16, Hkv=2, dqk=192, dv=128, window=128, dtype=1, swa=True):
+    if swa:
+        return lib.sinkattn_prefill_swa(q, k, v, sink, o, lse, B, T, Hq, Hkv, dqk, dv, window,
+                                        0.0, dtype, None)
+    return lib.sinkattn_prefill_global(q, k, v, sink, o, lse, B, T, Hq, Hkv, dqk, dv, 0.0, dtype,
+                                       None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, q=None) == NULL
+    assert prefill(lib, sink=None) == NULL
+    assert prefill(lib, dtype=7) == DTYPE
+    assert prefill(lib, Hq=15) == SHAPE          # Hq % Hkv
+    assert prefill(lib, Hkv=0) == SHAPE
+    assert prefill(lib, dqk=128) == UNSUP
+    assert prefill(lib, dv=192) == UNSUP
+    assert prefill(lib, Hq=8, Hkv=2) == UNSUP    # bf16 needs groups of 8 heads
+    assert prefill(lib, window=0) == SHAPE
+    assert prefill(lib, T=-1) == SHAPE
+    assert prefill(lib, B=0) == OK               # nothing to do, no HIP call
+    assert prefill(lib, T=0, swa=False) == OK
+    # o overlapping q
+    assert prefill(lib, o=P(FAKE[0].value + 64)) == ALIAS
+    assert prefill(lib, lse=P(FAKE[4].value + 8)) == ALIAS
+
+
+def decode(lib, *, kind=0, cap=128, max_len=1000, B=2, Hq=16, Hkv=2, window=128, splits=0,
+           ws=None, ws_bytes=0, dtype=1, o=FAKE[9], q=FAKE[0], cache_len=FAKE[5], k_cache=FAKE[3]):
+    return lib.sinkattn_decode(q, FAKE[1], FAKE[2], k_cache, P(13 << 36), kind, cap,
+                               cache_len, max_len, FAKE[6], o, B, Hq, Hkv, 192, 128, window, 0.0,
+                               splits, ws, ws_bytes, dtype, None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, q=None) == NULL
+    assert decode(lib, cache_len=None) == NULL
+    assert decode(lib, kind=5) == UNSUP
+    assert decode(lib, kind=0, cap=64) == CAP         # ring smaller than the window
+    assert decode(lib, kind=0, window=0) == SHAPE
+    assert decode(lib, kind=1, cap=1000, max_len=1000) == CAP  # decode writes index max_len
+    assert decode(lib, kind=1, cap=4096, max_len=1000, splits=4) == WS
+    assert decode(lib, kind=1, cap=4096, max_len=1000, splits=4, ws=FAKE[10],
+                  ws_bytes=lib.sinkattn_decode_workspace_bytes(2, 16, 128, 1, 4) - 4) == WS
+    assert decode(lib, max_len=-1) == SHAPE
+    assert decode(lib, dtype=2) == DTYPE
+    assert decode(lib, B=0) == OK
+    assert decode(lib, o=P(FAKE[0].value + 2)) == ALIAS
+
+
+def test_verify_validation(lib):
+    def verify(nq=4, Hq=64, Hkv=4, kind=1, cap=20000, max_len=16384):
+        return lib.sinkattn_verify(FAKE[0], FAKE[1], FAKE[2], FAKE[3], P(13 << 36), kind, cap,
+                                   FAKE[5], max_len, FAKE[6], FAKE[9], 2, nq, Hq, Hkv, 192, 128, 0,
+                                   0.0, 1, None, 0, 1, None)
+    assert verify(nq=0) == SHAPE
+    assert verify(nq=9) == SHAPE
+    assert verify(nq=5) == UNSUP                  # 5 * 16 columns > 64 on the bf16 path
+    assert verify(max_len=20001) == CAP
+    assert verify(kind=0, cap=100) == SHAPE       # ring needs a window >= 1 (window=0 here)
+
+
+def test_rope_and_append_validation(lib):
+    r = lib.sinkattn_rope_partial
+    assert r(None, 1, 10, 8, 192, 64, FAKE[1], 1e4, 0, None) == NULL
+    assert r(FAKE[0], 1, 10, 8, 192, 63, FAKE[1], 1e4, 0, None) == SHAPE   # odd rope_dim
+    assert r(FAKE[0], 1, 10, 8, 192, 256, FAKE[1], 1e4, 0, None) == SHAPE  # > head_dim
+    assert r(FAKE[0], 1, 10, 8, 192, 64, FAKE[1], -1.0, 0, None) == SHAPE
+    assert r(FAKE[0], 1, 10, 8, 192, 64, FAKE[1], 1e4, 2, None) == SHAPE
+    assert r(FAKE[0], 9, 10, 8, 192, 64, FAKE[1], 1e4, 0, None) == DTYPE
+    assert r(FAKE[0], 1, 0, 8, 192, 64, FAKE[1], 1e4, 0, None) == OK
+    a = lib.sinkattn_kv_append
+    assert a(FAKE[0], FAKE[1], FAKE[2], FAKE[3], 0, 128, None, None, 2, 4, 8, 192, 128, 1,
+             None) == NULL
+    assert a(FAKE[0], FAKE[1], FAKE[2], FAKE[3], 3, 128, FAKE[4], None, 2, 4, 8, 192, 128, 1,
+             None) == UNSUP
+    assert a(FAKE[0], FAKE[1], FAKE[2], FAKE[3], 0, 128, FAKE[4], None, 0, 4, 8, 192, 128, 1,
+             None) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 8, 192)
+    with pytest.raises(ops.SinkAttnError):
+        ops.prefill_swa(q, q[:, :, :1], torch.zeros(1, 4, 1, 128), torch.zeros(8))
