@@ -1,0 +1,476 @@
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others] [--no-cpu]
+
+Headline workload (one step): the sliding-window prefill layer of the report's
+Table 1 at T = 32768 -- partial RoPE (64 dims, base 1e4) on q [1,32768,64,192]
+and k [1,32768,8,192], then causal sink attention with W = 128 over v
+[1,32768,8,128] -- on synthetic seeded bf16 inputs already resident in HBM.
+``value`` is in-window prefill TFLOP/s: (visible (query, key) pairs x 64 query
+heads x 640 FLOP) per step divided by the step time.
+
+The same JSON line carries the roofline of the dominant kernel (the prefill
+kernel, HBM bound: 1.5099e9 algorithmic bytes per launch), the CPU oracle timed
+on a bounded sample of the same workload, and the other four workloads measured
+alongside (global prefill, hybrid-block decode, speculative verify; the tiny
+fp32 case is parity only).  Only rank 0 of one process runs: the build uses a
+single GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA, published
+FLOP_PER_PAIR_HEAD = 2 * 192 + 2 * 128
+METRIC = "prefill TFLOP/s (in-window) & %MFMA peak; decode KV GB/s & %HBM peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--only", default="", help="comma list of: swa,global,decode,verify")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def swa_pairs(T: int, W: int) -> int:
+    """Visible (query, key) pairs of a causal window of W keys including self:
+    sum over queries i < T of min(i + 1, W)."""
+    if T <= W:
+        return T * (T + 1) // 2
+    return W * (W + 1) // 2 + (T - W) * W
+
+
+def global_pairs(T: int) -> int:
+    return T * (T + 1) // 2
+
+
+class Timer:
+    """HIP events around launches on torch's current stream (where the kernels run)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        self.a = self.torch.cuda.Event(enable_timing=True)
+        self.b = self.torch.cuda.Event(enable_timing=True)
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.pairs.append((self.a, self.b))
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def flush_caches(torch, buf):
+    """Write a 512 MB buffer so L2 and the 256 MB Infinity Cache hold none of the inputs."""
+    buf.add_(1)
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ["sliding_window_sink_amd/csrc/prefill.hip", "sliding_window_sink_amd/csrc/common.h"]
+
+
+def traffic_from_profile(sha: str, launches_bytes: float):
+    """HBM bytes per launch of the prefill kernel from committed rocprofv3 --pmc
+    counters, if they were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "prefill_swa_T32768_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("kernel_source_sha") != sha:
+        return None
+    return float(d["hbm_bytes_per_launch"])
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def run_swa_prefill(torch, ops, synth, steps, warmup, dev):
+    w = synth.WORKLOADS[2]
+    B, T, Hq, Hkv = w.B, w.T, w.Hq, w.Hkv
+    q = synth.device_normal(w.seed, (B, T, Hq, 192), device=dev)
+    k = synth.device_normal(w.seed + 1, (B, T, Hkv, 192), device=dev)
+    v = synth.device_normal(w.seed + 2, (B, T, Hkv, 128), device=dev)
+    sink = synth.device_normal(w.seed + 3, (Hq,), torch.float32, device=dev)
+    pos = synth.positions(B, T).to(dev)
+    o = torch.empty(B, T, Hq, 128, dtype=torch.bfloat16, device=dev)
+
+    kt, rt = Timer(torch), Timer(torch)
+
+    def step(timed):
+        # q and k are rotated in place every step: the same work each time
+        if timed:
+            with rt:
+                ops.rope_partial(q, pos, w.base)
+                ops.rope_partial(k, pos, w.base)
+            with kt:
+                ops.prefill_swa(q, k, v, sink, window=w.window, out=o)
+        else:
+            ops.rope_partial(q, pos, w.base)
+            ops.rope_partial(k, pos, w.base)
+            ops.prefill_swa(q, k, v, sink, window=w.window, out=o)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pairs = swa_pairs(T, w.window) * B
+    flops = pairs * Hq * FLOP_PER_PAIR_HEAD
+    bytes_kernel = B * T * (Hq + Hkv) * (192 + 128) * 2  # Q,K,V read + O write
+    kern_ms = kt.mean_ms()
+    rope_ms = rt.mean_ms()
+    res = dict(wall_s=wall, ms_per_step=wall * 1e3 / steps, flops=flops, pairs=pairs,
+               kernel_ms=kern_ms, rope_ms=rope_ms, kernel_bytes=bytes_kernel,
+               rope_bytes=B * T * (Hq + Hkv) * 64 * 2 * 2)
+    inputs = dict(q=q, k=k, v=v, sink=sink, o=o, w=w)
+    return res, inputs
+
+
+def run_global_prefill(torch, ops, synth, dev, reps=5):
+    w = synth.WORKLOADS[3]
+    B, T, Hq, Hkv = w.B, w.T, w.Hq, w.Hkv
+    q = synth.device_normal(w.seed, (B, T, Hq, 192), device=dev)
+    k = synth.device_normal(w.seed + 1, (B, T, Hkv, 192), device=dev)
+    v = synth.device_normal(w.seed + 2, (B, T, Hkv, 128), device=dev)
+    sink = synth.device_normal(w.seed + 3, (Hq,), torch.float32, device=dev)
+    pos = synth.positions(B, T).to(dev)
+    o = torch.empty(B, T, Hq, 128, dtype=torch.bfloat16, device=dev)
+    kt, rt = Timer(torch), Timer(torch)
+    ops.prefill_global(q, k, v, sink, out=o)  # warm-up
+    for _ in range(reps):
+        with rt:
+            ops.rope_partial(q, pos, w.base)
+            ops.rope_partial(k, pos, w.base)
+        with kt:
+            ops.prefill_global(q, k, v, sink, out=o)
+    kms, rms = kt.mean_ms(), rt.mean_ms()
+    flops = global_pairs(T) * B * Hq * FLOP_PER_PAIR_HEAD
+    del q, k, v, o
+    return dict(workload=w.name, kernel_ms=kms, rope_ms=rms, step_ms=kms + rms,
+                tflops_kernel=flops / kms / 1e9, tflops_step=flops / (kms + rms) / 1e9,
+                mfma_frac_kernel=flops / kms / 1e9 / PEAK_BF16_TFLOPS, flops=flops)
+
+
+def _graph_time(torch, fn, reps=20):
+    """Capture fn (a sequence of launches) in a HIP graph, replay, time with events."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    for _ in range(reps):
+        with t:
+            g.replay()
+    return t.mean_ms(), g
+
+
+def run_hybrid_decode(torch, ops, synth, dev):
+    w = synth.WORKLOADS[4]
+    B, Hq = w.B, 64
+    g = synth.generator(w.seed)
+    cl = synth.cache_lengths(g, B, 16384, 131072)
+    cap = 131072 + 8
+    rings = []
+    for layer in range(5):
+        s0 = w.seed * 100 + layer * 10
+        rings.append(dict(
+            q=synth.device_normal(s0, (B, Hq, 192), device=dev),
+            kn=synth.device_normal(s0 + 1, (B, 8, 192), device=dev),
+            vn=synth.device_normal(s0 + 2, (B, 8, 128), device=dev),
+            kc=synth.device_normal(s0 + 3, (B, 8, 128, 192), device=dev),
+            vc=synth.device_normal(s0 + 4, (B, 8, 128, 128), device=dev),
+            sink=synth.device_normal(s0 + 5, (Hq,), torch.float32, device=dev),
+            o=torch.empty(B, Hq, 128, dtype=torch.bfloat16, device=dev)))
+    s0 = w.seed * 100 + 90
+    gl = dict(q=synth.device_normal(s0, (B, Hq, 192), device=dev),
+              kn=synth.device_normal(s0 + 1, (B, 4, 192), device=dev),
+              vn=synth.device_normal(s0 + 2, (B, 4, 128), device=dev),
+              kc=torch.empty(B, 4, cap, 192, dtype=torch.bfloat16, device=dev),
+              vc=torch.empty(B, 4, cap, 128, dtype=torch.bfloat16, device=dev),
+              sink=synth.device_normal(s0 + 5, (Hq,), torch.float32, device=dev),
+              o=torch.empty(B, Hq, 128, dtype=torch.bfloat16, device=dev))
+    for b in range(B):
+        L = int(cl[b])
+        synth.device_normal(s0 + 1000 + b, None, device=dev, out=gl["kc"][b, :, :L])
+        synth.device_normal(s0 + 2000 + b, None, device=dev, out=gl["vc"][b, :, :L])
+    cl_d = cl.to(dev)
+    max_len = int(cl.max())
+    ws = torch.empty(ops.decode_workspace_bytes(B, Hq, 1, 256) // 4, dtype=torch.float32,
+                     device=dev)
+
+    def swa(r):
+        ops.decode(r["q"], r["kn"], r["vn"], r["kc"], r["vc"], cl_d, r["sink"], ops.RING, 128,
+                   max_len, out=r["o"])
+
+    def glob():
+        ops.decode(gl["q"], gl["kn"], gl["vn"], gl["kc"], gl["vc"], cl_d, gl["sink"], ops.CONTIG,
+                   0, max_len, num_splits=0, workspace=ws, out=gl["o"])
+
+    def block():
+        for r in rings:
+            swa(r)
+        glob()
+
+    step_ms, _ = _graph_time(torch, block)
+    # per-layer times with the caches flushed in between (events around one layer)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ts, tg = Timer(torch), Timer(torch)
+    for _ in range(10):
+        flush_caches(torch, flush)
+        with ts:
+            swa(rings[0])
+        flush_caches(torch, flush)
+        with tg:
+            glob()
+    swa_ms, glob_ms = ts.mean_ms(), tg.mean_ms()
+    keys_g = int((cl.to(torch.int64) + 1).sum()) * 4
+    keys_s = B * 8 * 128
+    kv_g = keys_g * 640
+    kv_s = keys_s * 640
+    qo = B * Hq * (192 + 128) * 2
+    total_kv = 5 * kv_s + kv_g
+    total_bytes = total_kv + 6 * qo
+    gflops = 2 * keys_g * 16 * 320  # 16 query heads per KV head, 640 FLOP per pair
+    del gl, rings
+    return dict(workload=w.name, step_ms=step_ms, kv_bytes=total_kv, bytes=total_bytes,
+                kv_gbs=total_kv / step_ms / 1e6, hbm_frac=total_bytes / step_ms / 1e6 / PEAK_HBM_GBS,
+                swa_layer_ms=swa_ms, swa_layer_gbs=(kv_s + qo) / swa_ms / 1e6,
+                global_ms=glob_ms, global_gbs=(kv_g + qo) / glob_ms / 1e6,
+                global_hbm_frac=(kv_g + qo) / glob_ms / 1e6 / PEAK_HBM_GBS,
+                global_tflops=gflops / glob_ms / 1e9, mean_ctx=float(cl.double().mean()))
+
+
+def run_verify(torch, ops, synth, dev):
+    w = synth.WORKLOADS[5]
+    B, nq, Hq, L = w.B, w.T, 64, 16384
+    cap = L + 8
+    cl = torch.full((B,), L, dtype=torch.int32)
+    cl_d = cl.to(dev)
+    s0 = w.seed * 100
+    pos = synth.positions(B, nq, L).to(dev)
+    swa = dict(q=synth.device_normal(s0, (B, nq, Hq, 192), device=dev),
+               kn=synth.device_normal(s0 + 1, (B, nq, 8, 192), device=dev),
+               vn=synth.device_normal(s0 + 2, (B, nq, 8, 128), device=dev),
+               kc=synth.device_normal(s0 + 3, (B, 8, 128, 192), device=dev),
+               vc=synth.device_normal(s0 + 4, (B, 8, 128, 128), device=dev),
+               sink=synth.device_normal(s0 + 5, (Hq,), torch.float32, device=dev),
+               o=torch.empty(B, nq, Hq, 128, dtype=torch.bfloat16, device=dev))
+    gl = dict(q=synth.device_normal(s0 + 10, (B, nq, Hq, 192), device=dev),
+              kn=synth.device_normal(s0 + 11, (B, nq, 4, 192), device=dev),
+              vn=synth.device_normal(s0 + 12, (B, nq, 4, 128), device=dev),
+              kc=torch.empty(B, 4, cap, 192, dtype=torch.bfloat16, device=dev),
+              vc=torch.empty(B, 4, cap, 128, dtype=torch.bfloat16, device=dev),
+              sink=synth.device_normal(s0 + 15, (Hq,), torch.float32, device=dev),
+              o=torch.empty(B, nq, Hq, 128, dtype=torch.bfloat16, device=dev))
+    synth.device_normal(s0 + 13, None, device=dev, out=gl["kc"][:, :, :L])
+    synth.device_normal(s0 + 14, None, device=dev, out=gl["vc"][:, :, :L])
+    ws = torch.empty(ops.decode_workspace_bytes(B, Hq, nq, 256) // 4, dtype=torch.float32,
+                     device=dev)
+    # decode baseline for the verify/decode ratio: same caches, one query token
+    kc1 = gl["kc"]
+
+    def rope_new():
+        for d in (swa, gl):
+            ops.rope_partial(d["q"], pos, synth.BASE_SWA if d is swa else synth.BASE_GA)
+            ops.rope_partial(d["kn"], pos, synth.BASE_SWA if d is swa else synth.BASE_GA)
+
+    def v_swa():
+        ops.verify(swa["q"], swa["kn"], swa["vn"], swa["kc"], swa["vc"], cl_d, swa["sink"],
+                   ops.RING, 128, L, out=swa["o"])
+
+    def v_glob():
+        ops.verify(gl["q"], gl["kn"], gl["vn"], gl["kc"], gl["vc"], cl_d, gl["sink"], ops.CONTIG,
+                   0, L, num_splits=0, workspace=ws, out=gl["o"])
+
+    q1, kn1, vn1 = (gl["q"][:, 0:1].contiguous(), gl["kn"][:, 0:1].contiguous(),
+                    gl["vn"][:, 0:1].contiguous())
+    o1 = torch.empty(B, 1, Hq, 128, dtype=torch.bfloat16, device=dev)
+
+    def d_glob():
+        ops.verify(q1, kn1, vn1, kc1, gl["vc"], cl_d, gl["sink"], ops.CONTIG, 0, L,
+                   num_splits=0, workspace=ws, out=o1)
+
+    def step():
+        rope_new()
+        v_swa()
+        v_glob()
+
+    step_ms, _ = _graph_time(torch, step)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ts, tg, td = Timer(torch), Timer(torch), Timer(torch)
+    for _ in range(10):
+        flush_caches(torch, flush)
+        with ts:
+            v_swa()
+        flush_caches(torch, flush)
+        with tg:
+            v_glob()
+        flush_caches(torch, flush)
+        with td:
+            d_glob()
+    swa_ms, glob_ms, dec_ms = ts.mean_ms(), tg.mean_ms(), td.mean_ms()
+    kv_s = B * 8 * (127 + nq) * 640
+    kv_g = B * 4 * (L + nq) * 640
+    qo = B * nq * Hq * 640
+    del gl, swa
+    return dict(workload=w.name, step_ms=step_ms,
+                swa_ms=swa_ms, swa_gbs=(kv_s + qo) / swa_ms / 1e6,
+                global_ms=glob_ms, global_gbs=(kv_g + qo) / glob_ms / 1e6,
+                global_hbm_frac=(kv_g + qo) / glob_ms / 1e6 / PEAK_HBM_GBS,
+                global_decode1_ms=dec_ms, verify_over_decode=glob_ms / dec_ms,
+                kv_gbs=(kv_s + kv_g) / step_ms / 1e6)
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(torch, inputs, target_s: float):
+    """Time the CPU oracle (as it stands) on a bounded, contiguous block of query
+    tokens of the SWA workload: RoPE of those q rows and the k rows they see,
+    then sink attention for all 64 heads.  Rate in in-window TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    w = inputs["w"]
+    T, W = w.T, w.window
+
+    def sample(n_tok):
+        t0 = T // 2
+        rows = np.arange(t0, t0 + n_tok)
+        klo = t0 - W + 1
+        q = inputs["q"][0, t0:t0 + n_tok].float().cpu().double().numpy()
+        k = inputs["k"][0, klo:t0 + n_tok].float().cpu().double().numpy()
+        v = inputs["v"][0, klo:t0 + n_tok].float().cpu().double().numpy()
+        sink = inputs["sink"].cpu().double().numpy()
+        start = time.perf_counter()
+        qr = oracle.rope_partial(q, rows, w.base)
+        kr = oracle.rope_partial(k, np.arange(klo, t0 + n_tok), w.base)
+        oracle.sink_attention(qr, kr, v, rows, np.arange(klo, t0 + n_tok), sink, W)
+        return time.perf_counter() - start
+
+    n = 64
+    dt = sample(n)
+    n2 = int(min(T // 2 - W, max(n, n * target_s / max(dt, 1e-3))))
+    dt = sample(n2)
+    flops = n2 * W * w.Hq * FLOP_PER_PAIR_HEAD
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d consecutive query tokens (positions %d..%d, 64 heads, W=128) of the "
+                      "T=32768 SWA prefill incl. RoPE of their q/k rows; %.1f s on the host"
+                      % (n2, T // 2, T // 2 + n2 - 1, dt),
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs no multi-GPU path "
+              "(collectives/sharding are a design note); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from sliding_window_sink_amd import ops, synth
+    ops.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    only = set(args.only.split(",")) if args.only else {"swa", "global", "decode", "verify"}
+
+    log("[bench] SWA prefill T=32768: warmup %d, steps %d" % (args.warmup, args.steps))
+    res, inputs = run_swa_prefill(torch, ops, synth, args.steps, args.warmup, dev)
+    ms = res["ms_per_step"]
+    value = res["flops"] / (ms * 1e-3) / 1e12
+    sha = source_sha(PREFILL_SOURCES)
+    kern_s = res["kernel_ms"] * 1e-3
+    achieved = res["kernel_bytes"] / kern_s / 1e9
+    traffic = traffic_from_profile(sha, res["kernel_bytes"])
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 activations, N(0,1) fp32 sinks; no weights)",
+        "config": {"workload": "swa_prefill_layer_bf16", "B": 1, "T": 32768, "q_heads": 64,
+                   "kv_heads": 8, "d_qk": 192, "d_v": 128, "window": 128,
+                   "rope": "64 dims, base 1e4, in place on q and k",
+                   "step": "rope(q) + rope(k) + prefill_swa", "parallelism": "single GPU"},
+        "mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": "prefill_bf16_kernel<windowed>", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "algorithmic_bytes": res["kernel_bytes"],
+                     "avg_launch_ms": round(res["kernel_ms"], 4),
+                     "kernel_tflops": round(res["flops"] / kern_s / 1e12, 2),
+                     "kernel_source_sha": sha},
+        "rope": {"avg_ms": round(res["rope_ms"], 4), "bytes": res["rope_bytes"],
+                 "gbs": round(res["rope_bytes"] / (res["rope_ms"] * 1e-3) / 1e9, 1)},
+    }
+    others = {}
+    if not args.no_others:
+        if "global" in only:
+            log("[bench] global prefill T=32768")
+            others["global_prefill"] = run_global_prefill(torch, ops, synth, dev)
+        if "decode" in only:
+            log("[bench] hybrid-block decode B=32")
+            others["hybrid_decode"] = run_hybrid_decode(torch, ops, synth, dev)
+        if "verify" in only:
+            log("[bench] speculative verify B=64 nq=4")
+            others["verify"] = run_verify(torch, ops, synth, dev)
+        for v in others.values():
+            for kk, vv in list(v.items()):
+                if isinstance(vv, float):
+                    v[kk] = round(vv, 5)
+    line["other_workloads"] = others
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(torch, inputs, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -172,3 +172,23 @@ def fill_contig(layer: CachedLayer, cache_len: torch.Tensor, cap: int, Hkv: int,
         kc[b, :, L - rows:L] = layer.k_hist[b].permute(1, 0, 2)
         vc[b, :, L - rows:L] = layer.v_hist[b].permute(1, 0, 2)
     return kc, vc
+
+
+def device_normal(seed: int, shape, dtype=torch.bfloat16, device="cuda", std: float = 1.0,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """N(0, std^2) drawn with a seeded generator ON the device (for buffers of
+    gigabytes, where a CPU draw would take minutes), cast (RNE) to ``dtype``.
+    Draws happen in slices of the leading dim so the fp32 temporary stays small."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=device)
+    n0 = out.shape[0]
+    per = max(1, (1 << 27) // max(1, out[0].numel()))
+    for i in range(0, n0, per):
+        j = min(n0, i + per)
+        x = torch.randn(out[i:j].shape, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        out[i:j].copy_(x)
+    return out
