@@ -103,6 +103,20 @@ int sinkattn_prefill_swa(const void *q, const void *k, const void *v, const floa
                          void *o, float *lse, int B, int T, int Hq, int Hkv, int dqk, int dv,
                          int window, float scale, int dtype, void *stream);
 
+/*
+ * Sliding-window prefill with the partial RoPE fused into the loads: the result
+ * equals sinkattn_rope_partial(q, positions 0..T-1), the same for k, then
+ * sinkattn_prefill_swa -- bit for bit -- without writing the rotated q.
+ * q and k are read-only (un-rotated); if k_rot is non-NULL the rotated k is
+ * written there ([B,T,Hkv,192], e.g. straight into a KV cache; it must not
+ * overlap any input).  Supported: bf16, rope_dim == 64 (interleaved pairs,
+ * Section 2.1), 1 <= window <= 129 (SINKATTN_ERR_UNSUPPORTED otherwise).
+ */
+int sinkattn_prefill_swa_rope(const void *q, const void *k, const void *v, const float *sink,
+                              void *o, float *lse, void *k_rot, int B, int T, int Hq, int Hkv,
+                              int dqk, int dv, int window, float scale, int rope_dim,
+                              double rope_base, int dtype, void *stream);
+
 /* Causal prefill over the full context (global-attention layers, Table 1). */
 int sinkattn_prefill_global(const void *q, const void *k, const void *v, const float *sink,
                             void *o, float *lse, int B, int T, int Hq, int Hkv, int dqk,

@@ -6,4 +6,5 @@ is loaded on first use; nothing here computes on the CPU.
 """
 from .ops import (BF16, CONTIG, F32, HALF, INTERLEAVED, RING, SinkAttnError,  # noqa: F401
                   SinkAttnUnavailable, abi_version, decode, decode_workspace_bytes,
-                  default_scale, kv_append, prefill_global, prefill_swa, rope_partial, verify)
+                  default_scale, kv_append, prefill_global, prefill_swa, prefill_swa_rope,
+                  rope_partial, verify)

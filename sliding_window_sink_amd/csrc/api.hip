@@ -90,8 +90,11 @@ int prefill_common(const void *q, const void *k, const void *v, const float *sin
     PrefillArgs a{q, k, v, sink, o, lse, B, T, Hq, Hkv, window,
                   scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)dqk))};
     hipStream_t s = (hipStream_t)stream;
-    return status_from_hip(dtype == SINKATTN_BF16 ? launch_prefill_bf16(a, s)
-                                                  : launch_prefill_f32(a, s));
+    if (dtype != SINKATTN_BF16)
+        return status_from_hip(launch_prefill_f32(a, s));
+    if (window > 0 && window <= kSwaMaxWindow)
+        return status_from_hip(launch_prefill_swa_persistent(a, 0.0, nullptr, false, s));
+    return status_from_hip(launch_prefill_bf16(a, s));
 }
 
 size_t ws_bytes_for(int B, int Hq, int dv, int nq, int splits) {
@@ -257,6 +260,42 @@ int sinkattn_prefill_swa(const void *q, const void *k, const void *v, const floa
     }
     return prefill_common(q, k, v, sink, o, lse, B, T, Hq, Hkv, dqk, dv, window, scale, dtype,
                           stream);
+}
+
+int sinkattn_prefill_swa_rope(const void *q, const void *k, const void *v, const float *sink,
+                              void *o, float *lse, void *k_rot, int B, int T, int Hq, int Hkv,
+                              int dqk, int dv, int window, float scale, int rope_dim,
+                              double rope_base, int dtype, void *stream) {
+    int st = check_heads(Hq, Hkv, dqk, dv, dtype);
+    if (st)
+        return st;
+    if (!q || !k || !v || !sink || !o)
+        return SINKATTN_ERR_NULL_PTR;
+    if (B < 0 || T < 0 || window < 1 || !(rope_base > 0.0) || !std::isfinite(rope_base) ||
+        rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > dqk)
+        return SINKATTN_ERR_SHAPE;
+    if (dtype != SINKATTN_BF16 || rope_dim != 64 || window > kSwaMaxWindow)
+        return SINKATTN_ERR_UNSUPPORTED;
+    if ((int64_t)B * T * Hq > INT_MAX || (int64_t)B * T > INT_MAX / kDqk)
+        return SINKATTN_ERR_SHAPE;
+    const size_t es = esize(dtype);
+    const size_t qn = (size_t)B * T * Hq * kDqk * es, kn = (size_t)B * T * Hkv * kDqk * es;
+    const size_t vn = (size_t)B * T * Hkv * kDv * es, on = (size_t)B * T * Hq * kDv * es;
+    const size_t ln = lse ? (size_t)B * Hq * T * 4 : 0;
+    const void *ins[3] = {q, k, v};
+    const size_t insz[3] = {qn, kn, vn};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(o, on, ins[i], insz[i]) || overlaps(lse, ln, ins[i], insz[i]) ||
+            overlaps(k_rot, kn, ins[i], insz[i]))
+            return SINKATTN_ERR_ALIAS;
+    if (overlaps(lse, ln, o, on) || overlaps(k_rot, kn, o, on) || overlaps(k_rot, kn, lse, ln))
+        return SINKATTN_ERR_ALIAS;
+    if ((size_t)B * T == 0)
+        return SINKATTN_OK;
+    PrefillArgs a{q, k, v, sink, o, lse, B, T, Hq, Hkv, window,
+                  scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)dqk))};
+    return status_from_hip(
+        launch_prefill_swa_persistent(a, rope_base, k_rot, true, (hipStream_t)stream));
 }
 
 int sinkattn_prefill_global(const void *q, const void *k, const void *v, const float *sink,

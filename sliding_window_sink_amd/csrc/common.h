@@ -46,6 +46,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- buffer (descriptor) memory access ----
+// A raw buffer descriptor covers [base, base + bytes); the hardware returns 0
+// for loads and drops stores whose offset falls outside it, so ragged tails
+// need no branches, and addresses are a wave-uniform descriptor plus a 32-bit
+// per-lane byte offset.  Word 3 (0x00020000) is the raw-buffer format of gfx9.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ BufRsrc make_buf(const void *base, uint64_t bytes) {
+    const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+                                             0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(BufRsrc r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(BufRsrc r, uint32_t off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(BufRsrc r, uint32_t off, uint2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
+
+// Online-softmax rescale threshold (log2 units): the running max is only
+// raised when a block's max exceeds it by more than this, so exp2(x - m) stays
+// <= 2^8 and the accumulator rescale is rare.  Any m works (it cancels in
+// acc / l); this only trades a bounded growth of p for fewer rescales.
+constexpr float kRescaleSlack = 8.0f;
+
 // Max over the two 32-lane halves of a wave (lanes l and l^32 hold the same column).
 __device__ __forceinline__ float max_across_halves(float x) {
     return fmaxf(x, __shfl_xor(x, 32, 64));
@@ -70,6 +100,62 @@ __host__ __device__ __forceinline__ int row_of_key(int kk) {
 }
 __host__ __device__ __forceinline__ int key_of_row(int r) {
     return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
+
+// ---- partial RoPE (shared by the standalone kernel and the fused prefill) ----
+// theta_c = base^(-2c/rope_dim), angle = pos * theta_c, both in fp64 (an fp32
+// angle is off by ~1e-3 rad near position 1e5); cos/sin rounded to fp32.
+__device__ __forceinline__ double rope_inv_freq(double base, int c, int rope_dim) {
+    return pow(base, -2.0 * (double)c / (double)rope_dim);
+}
+// cos/sin of the fp64 angle p * inv_freq.  The angle is reduced modulo 2*pi
+// first (Cody-Waite, two-part constant) so sincos only ever sees |r| <= pi:
+// large angles (position 1e5 at theta_0 = 1) otherwise take the slow
+// wide-argument path.
+__device__ __forceinline__ double2 rope_sincos64(int p, double inv_freq) {
+    const double two_pi_hi = 6.283185307179586232e+00;
+    const double two_pi_lo = 2.449293598294706414e-16;
+    const double inv_two_pi = 1.591549430918953358e-01;
+    const double phi = (double)p * inv_freq;
+    const double kq = rint(phi * inv_two_pi);
+    double red = fma(-kq, two_pi_hi, phi);
+    red = fma(-kq, two_pi_lo, red);
+    double sn, cn;
+    sincos(red, &sn, &cn);
+    return make_double2(cn, sn);
+}
+// A position is split as p = hi + lo with hi = 32*floor(p/32), lo = p mod 32; the
+// two rotations compose in fp64 and the result is rounded once to fp32.  Every
+// kernel (the standalone RoPE and the fused prefill, which tabulates the lo part
+// once and the hi part once per 32 tokens) evaluates exactly this expression, so
+// their results agree bit for bit.
+__device__ __forceinline__ float2 rope_compose(double2 hi, double2 lo) {
+    const double c = __fma_rn(hi.x, lo.x, -__dmul_rn(hi.y, lo.y));
+    const double s = __fma_rn(hi.y, lo.x, __dmul_rn(hi.x, lo.y));
+    return make_float2((float)c, (float)s);
+}
+__device__ __forceinline__ float2 rope_cos_sin(int pos, double inv_freq) {
+    return rope_compose(rope_sincos64(pos & ~31, inv_freq), rope_sincos64(pos & 31, inv_freq));
+}
+// Rotate the pair (x0, x1) by the angle whose (cos, sin) is cs, in fp32, with an
+// explicit operation order so every kernel rounds identically.
+__device__ __forceinline__ void rope_pair(float x0, float x1, float2 cs, float &y0, float &y1) {
+    y0 = __fmaf_rn(x0, cs.x, -__fmul_rn(x1, cs.y));
+    y1 = __fmaf_rn(x0, cs.y, __fmul_rn(x1, cs.x));
+}
+// Rotate the 4 interleaved pairs held in 8 bf16 (one 16-byte chunk); cs[p] is the
+// (cos, sin) of pair p of the chunk.
+__device__ __forceinline__ uint4 rope_chunk_bf16(uint4 x, const float2 *cs) {
+    uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float x0 = bf16_bits_to_f32((uint16_t)(w[p] & 0xffffu));
+        const float x1 = bf16_bits_to_f32((uint16_t)(w[p] >> 16));
+        float y0, y1;
+        rope_pair(x0, x1, cs[p], y0, y1);
+        w[p] = pack_bf16x2(y0, y1);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 }  // namespace sinkattn

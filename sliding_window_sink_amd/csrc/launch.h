@@ -49,6 +49,12 @@ hipError_t launch_rope(void *x, int bf16, int64_t n_tok, int n_heads, int head_d
                        const int32_t *pos, double base, int style, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, hipStream_t s);
+// Sliding-window prefill for window <= kSwaMaxWindow (bf16), optionally applying
+// partial RoPE (64 dims, interleaved, base rope_base) to q and k on load and
+// writing the rotated k to k_rot (may be null).
+constexpr int kSwaMaxWindow = 129;
+hipError_t launch_prefill_swa_persistent(const PrefillArgs &a, double rope_base, void *k_rot,
+                                         bool rope, hipStream_t s);
 hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s);
 hipError_t launch_cached_f32(const CachedArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int bf16, hipStream_t s);

@@ -1,0 +1,376 @@
+// prefill_swa.hip -- persistent sliding-window sink-attention prefill (gfx950, bf16).
+//
+// The operation is that of the MiMo-V2-Flash Technical Report, Section 2.2
+// (sink softmax, equations 1-4) restricted to a window of W <= 129 keys
+// (Table 1: W = 128): query i sees keys i-W+1 .. i.  With the rope option it
+// also applies the partial RoPE of Section 2.1 (first 64 dims, interleaved
+// pairs, base from Section 3.2) to q and k as they are loaded, giving the same
+// bits as rotating q and k first with the standalone RoPE kernel.
+//
+// Why a persistent kernel: a sliding-window layer is HBM bound (about 114
+// FLOP per byte, below the MI355X ridge), and its traffic is dominated by
+// reading Q and writing O once.  Each workgroup therefore walks a contiguous
+// run of 32-token tiles of one KV group and overlaps everything it can:
+//   - the last 5 key blocks (32 keys each) of the window live in a 6-slot LDS
+//     ring, so every K/V row is fetched from memory once per run, not once per
+//     tile (a 32-token tile sees 159 keys);
+//   - while tile i is computed, the next tile's Q (into registers) and its new
+//     key block (into registers, then into the free ring slot) are in flight;
+//   - one barrier per tile publishes the new key block.
+// All global traffic goes through raw buffer descriptors (a wave-uniform base
+// for the run plus a 32-bit lane offset): rows past the end of the sequence
+// read as zero and their stores are dropped by the hardware, so there are no
+// per-lane branches around loads and no 64-bit address registers to spill.
+//
+// Inside a tile: wave w owns query head 8*part + w; the 32 tokens are the MFMA
+// columns; S^T = K Q^T with K rows permuted so register i of lane half hh holds
+// key 16*hh + i; the online softmax is seeded with the sink; O^T += V^T P^T
+// reads V^T from LDS.  The V^T rows are laid out so that each lane ends up
+// holding runs of 8 consecutive output dims (16-byte stores).
+//
+// Grid: (batch, KV group, head part) units x runs, unit = blockIdx % units, so
+// each XCD keeps whole runs of one KV group in its L2.  One workgroup per CU
+// (8 waves, 2 per SIMD, ~151 KB of LDS).
+#include <algorithm>
+
+#include "common.h"
+
+namespace sinkattn {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTq = 32;
+constexpr int kKb = 32;
+constexpr int kSlots = 6;
+constexpr int kKPitch = kDqk + 8;   // 400-byte LDS rows for K
+constexpr int kVPitch = kKb + 8;    // 80-byte LDS rows for V^T
+constexpr int kKChunks = kKb * kDqk / 8;  // 768 16-byte pieces per key block
+constexpr int kVChunks = kKb * kDv / 8;   // 512
+constexpr int kPairs = 32;          // rope_dim / 2 with rope_dim = 64
+static_assert(kVChunks == kThreads, "one V piece per thread");
+
+struct SwaSmem {
+    uint16_t k[kSlots][kKb * kKPitch];
+    uint16_t vt[kSlots][kDv * kVPitch];
+    // RoPE: rotation by (p mod 32) * theta_c for the 32 offsets (built once; pair
+    // major, so the 32 lanes of a wave -- one token each -- read consecutive
+    // entries), and by 32*floor(p/32) * theta_c for one block (double buffered)
+    double2 lo_rot[kPairs][kTq];
+    double2 hi_rot[2][kPairs];
+    double inv_freq[kPairs];
+};
+
+struct SwaRope {
+    double base;
+    uint16_t *k_rot;  // optional copy of rotated k [B,T,Hkv,192]
+};
+
+// V^T LDS row holding output dim d.  Block db, C-row rho = 8a + 4hh + e of the PV
+// accumulators holds dim 32a + 16(db/2) + 8hh + 4(db%2) + e, so for each (a, db/2)
+// a lane owns 8 consecutive dims and the two lane halves are adjacent.
+__device__ __forceinline__ int pv_row_of_dim(int d) {
+    const int a = d >> 5, j = (d >> 4) & 1, hh = (d >> 3) & 1, dbl = (d >> 2) & 1, e = d & 3;
+    return 32 * (2 * j + dbl) + 8 * a + 4 * hh + e;
+}
+
+template <bool kRope>
+__global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, SwaRope rp,
+                                                                int n_units, int n_tiles,
+                                                                int tiles_per_run,
+                                                                float scale_log2) {
+    __shared__ SwaSmem sm;
+    const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, window = a.window;
+    const int group = Hq / Hkv;
+    const int parts = group / kWaves;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 31, hh = lane >> 5;
+    const int unit = blockIdx.x % n_units;
+    const int run = blockIdx.x / n_units;
+    const int part = unit % parts;
+    const int g = (unit / parts) % Hkv;
+    const int b = unit / (parts * Hkv);
+    const int h = g * group + part * kWaves + wave;
+    const int tile_begin = run * tiles_per_run;
+    const int tile_end = min(n_tiles, tile_begin + tiles_per_run);
+    if (tile_begin >= tile_end)
+        return;
+
+    auto first_block = [&](int t0) { return max(0, t0 - window + 1) / kKb; };
+
+    // Descriptors for this run: every token it touches is >= tbase.
+    const int tbase = first_block(tile_begin * kTq) * kKb;
+    const size_t row0 = (size_t)b * T + tbase;
+    const uint64_t nrows = (uint64_t)(T - tbase);
+    const uint32_t qrow = (uint32_t)Hq * kDqk * 2, orow = (uint32_t)Hq * kDv * 2;
+    const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
+    const BufRsrc qbuf = make_buf((const uint16_t *)a.q + row0 * Hq * kDqk, nrows * qrow);
+    const BufRsrc kbuf = make_buf((const uint16_t *)a.k + row0 * Hkv * kDqk, nrows * krow);
+    const BufRsrc vbuf = make_buf((const uint16_t *)a.v + row0 * Hkv * kDv, nrows * vrow);
+    const BufRsrc obuf = make_buf((uint16_t *)a.o + row0 * Hq * kDv, nrows * orow);
+    const bool write_krot = kRope && rp.k_rot != nullptr && part == 0;
+    const BufRsrc krbuf = make_buf(write_krot ? rp.k_rot + row0 * Hkv * kDqk : (uint16_t *)a.k,
+                                   write_krot ? nrows * krow : 0);
+    const uint32_t qcol = (uint32_t)h * kDqk * 2, kcol = (uint32_t)g * kDqk * 2,
+                   vcol = (uint32_t)g * kDv * 2, ocol = (uint32_t)h * kDv * 2;
+
+    if (kRope) {
+        if (tid < kPairs)
+            sm.inv_freq[tid] = rope_inv_freq(rp.base, tid, 2 * kPairs);
+        __syncthreads();
+        for (int idx = tid; idx < kTq * kPairs; idx += kThreads)
+            sm.lo_rot[idx / kTq][idx % kTq] = rope_sincos64(idx % kTq, sm.inv_freq[idx / kTq]);
+    }
+    // hi_rot[buf] <- rotation by t * theta_c (t a multiple of 32), threads 0..31.
+    auto fill_hi = [&](int buf, int t) {
+        if (tid < kPairs)
+            sm.hi_rot[buf][tid] = rope_sincos64(t, sm.inv_freq[tid]);
+    };
+    // (cos, sin) of pairs c0..c0+3 of the token at offset j of the block in hi_rot[buf]
+    auto rot4 = [&](int buf, int j, int c0, float2 (&cs)[4]) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            cs[p] = rope_compose(sm.hi_rot[buf][c0 + p], sm.lo_rot[c0 + p][j]);
+    };
+
+    // ---- key blocks: global -> registers -> (rotate) -> LDS ring slot ----
+    auto load_block = [&](int jb, uint4 (&kreg)[2], uint4 &vreg) {
+        const uint32_t rel = (uint32_t)(jb * kKb - tbase);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int c = tid + u * kThreads;
+            if (u == 0 || c < kKChunks)  // wave-uniform: waves 0..3 take a second piece
+                kreg[u] = buf_load16(kbuf, (rel + c / (kDqk / 8)) * krow + kcol +
+                                               (uint32_t)(c % (kDqk / 8)) * 16);
+        }
+        vreg = buf_load16(vbuf, (rel + tid / (kDv / 8)) * vrow + vcol +
+                                    (uint32_t)(tid % (kDv / 8)) * 16);
+    };
+    // cs_buf: hi_rot buffer of the block's tokens (rope only); own: this run writes k_rot
+    auto store_block = [&](int jb, const uint4 (&kreg)[2], const uint4 &vreg, int cs_buf,
+                           bool own) {
+        const int slot = jb % kSlots;
+        const uint32_t rel = (uint32_t)(jb * kKb - tbase);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int c = tid + u * kThreads;
+            if (u == 0 || c < kKChunks) {
+                const int kk = c / (kDqk / 8), d = c % (kDqk / 8);
+                uint4 x = kreg[u];
+                if (kRope && d < 8) {
+                    float2 cs[4];
+                    rot4(cs_buf, kk, 4 * d, cs);
+                    x = rope_chunk_bf16(x, cs);
+                }
+                *(uint4 *)&sm.k[slot][row_of_key(kk) * kKPitch + d * 8] = x;
+                if (kRope && write_krot && own)
+                    buf_store16(krbuf, (rel + kk) * krow + kcol + (uint32_t)d * 16, x);
+            }
+        }
+        const int kk = tid / (kDv / 8), dc = tid % (kDv / 8);
+        const uint32_t w[4] = {vreg.x, vreg.y, vreg.z, vreg.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            sm.vt[slot][pv_row_of_dim(dc * 8 + j) * kVPitch + kk] =
+                (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+    };
+    // Q^T operand of one tile: k-step s, half hh -> dims (2s+hh)*8 .. +7 of token t0+r.
+    auto load_q = [&](int t0, uint4 (&qr)[kDqk / 16]) {
+        const uint32_t off = (uint32_t)(t0 + r - tbase) * qrow + qcol + (uint32_t)hh * 16;
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s)
+            qr[s] = buf_load16(qbuf, off + (uint32_t)s * 32);
+    };
+    auto rotate_q = [&](uint4 (&qr)[kDqk / 16], int cs_buf) {
+        if (kRope) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {  // dims < 64: chunks 2s+hh < 8
+                float2 cs[4];
+                rot4(cs_buf, r, 4 * (2 * s + hh), cs);
+                qr[s] = rope_chunk_bf16(qr[s], cs);
+            }
+        }
+    };
+
+    // ---- prologue: the first tile's window and Q; hi rotations of the next tiles ----
+    // hi_rot[i & 1] holds tile i's block; it is written two tiles ahead (at the
+    // end of tile i-2, or here) and published by that tile's closing barrier.
+    uint4 qcur[kDqk / 16];
+    {
+        const int t0 = tile_begin * kTq;
+        const int jlo = first_block(t0), jhi = t0 / kKb;
+        const int cb = tile_begin & 1;
+        for (int jb = jlo; jb <= jhi; ++jb) {
+            uint4 kreg[2], vreg;
+            if (kRope) {
+                fill_hi(cb, jb * kKb);
+                __syncthreads();
+            }
+            load_block(jb, kreg, vreg);
+            store_block(jb, kreg, vreg, cb, jb == jhi);
+            __syncthreads();
+        }
+        load_q(t0, qcur);
+        rotate_q(qcur, cb);  // hi_rot[cb] now holds block jhi = this tile
+        __syncthreads();
+        if (kRope && tile_begin + 1 < tile_end)
+            fill_hi(cb ^ 1, t0 + kTq);
+        __syncthreads();
+    }
+
+    const float sink2 = a.sink[h] * kLog2e;
+
+    for (int tile = tile_begin; tile < tile_end; ++tile) {
+        const int t0 = tile * kTq;
+        const int query = t0 + r;
+        const int jlo = first_block(t0), jhi = t0 / kKb;
+        const bool has_next = tile + 1 < tile_end;
+
+        uint4 kreg[2], vreg, qnext[kDqk / 16];
+        if (has_next) {
+            load_block(jhi + 1, kreg, vreg);
+            load_q(t0 + kTq, qnext);
+        }
+
+        float m = sink2;
+        float l = (hh == 0 && sink2 != -INFINITY) ? 1.f : 0.f;
+        f32x16 acc[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            acc[db] = f32x16{};
+
+        for (int jb = jlo; jb <= jhi; ++jb) {
+            const int kb = jb * kKb;
+            const uint16_t *ks = sm.k[jb % kSlots];
+            const uint16_t *vs = sm.vt[jb % kSlots];
+            f32x16 sc = f32x16{};
+            // K operands are read from LDS 4 k-steps at a time: the fence keeps the
+            // scheduler from hoisting all 12 reads (48 registers) above the MFMAs.
+#pragma unroll
+            for (int s0 = 0; s0 < kDqk / 16; s0 += 4) {
+#pragma unroll
+                for (int s = s0; s < s0 + 4; ++s) {
+                    const bf16x8 ka =
+                        as_bf16x8(*(const uint4 *)(ks + r * kKPitch + (2 * s + hh) * 8));
+                    sc = mfma32x32x16(ka, as_bf16x8(qcur[s]), sc);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // raw scores; masked ones -> -inf.  scale_log2 > 0, so the max of the raw
+            // scores times the scale is the max of the scaled logits.
+            const bool full = (kb + kKb - 1 <= t0) && (t0 + kTq - 1 - kb < window);
+            float bm = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (!full) {
+                    const int key = kb + 16 * hh + i;
+                    sc[i] = (key <= query && query - key < window) ? sc[i] : -INFINITY;
+                }
+                bm = fmaxf(bm, sc[i]);
+            }
+            bm = max_across_halves(bm) * scale_log2;
+            // raise m only when the block max passes it by more than the slack
+            const bool up = bm > m + kRescaleSlack || (m == -INFINITY && bm > -INFINITY);
+            const float mn = up ? bm : m;
+            const float alpha = up ? fast_exp2(m - mn) : 1.f;
+            m = mn;
+            const float mu = (mn == -INFINITY) ? 0.f : mn;
+            float ps = 0.f;
+            bf16x8 pb[2];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = fast_exp2(__fmaf_rn(sc[i], scale_log2, -mu));
+                ps += p;
+                pb[i >> 3][i & 7] = (__bf16)p;
+            }
+            l = __fmaf_rn(l, alpha, ps);
+            if (__builtin_amdgcn_ballot_w64(up) != 0) {  // wave-uniform rescale
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    acc[db] *= alpha;
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const bf16x8 va =
+                        as_bf16x8(*(const uint4 *)(vs + (32 * db + r) * kVPitch + 16 * hh + 8 * t));
+                    acc[db] = mfma32x32x16(va, pb[t], acc[db]);
+                }
+                if (db & 1)
+                    __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+
+        // The prefetched key block and Q are consumed before O is stored, so no
+        // wait on the prefetch can also end up waiting on the stores.
+        if (has_next) {
+            const int nb = (tile + 1) & 1;  // table of the next tile's tokens
+            store_block(jhi + 1, kreg, vreg, nb, true);
+            rotate_q(qnext, nb);
+        }
+
+        // epilogue: o = acc / l, 16-byte stores of 8 consecutive dims
+        const float lt = sum_across_halves(l);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const uint32_t obase = (uint32_t)(query - tbase) * orow + ocol + (uint32_t)hh * 16;
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const f32x16 &lo = acc[2 * j], &hi = acc[2 * j + 1];
+                uint4 w;
+                w.x = pack_bf16x2(lo[4 * aa + 0] * inv, lo[4 * aa + 1] * inv);
+                w.y = pack_bf16x2(lo[4 * aa + 2] * inv, lo[4 * aa + 3] * inv);
+                w.z = pack_bf16x2(hi[4 * aa + 0] * inv, hi[4 * aa + 1] * inv);
+                w.w = pack_bf16x2(hi[4 * aa + 2] * inv, hi[4 * aa + 3] * inv);
+                buf_store16(obuf, obase + (uint32_t)(64 * aa + 32 * j), w);
+            }
+        if (a.lse && hh == 0 && query < T) {
+            const float mu = (m == -INFINITY) ? 0.f : m;
+            a.lse[((size_t)b * Hq + h) * T + query] = lt > 0.f ? (mu + log2f(lt)) * kLn2 : -INFINITY;
+        }
+
+        if (has_next) {
+#pragma unroll
+            for (int s = 0; s < kDqk / 16; ++s)
+                qcur[s] = qnext[s];
+            if (kRope && tile + 2 < tile_end)
+                fill_hi(tile & 1, t0 + 2 * kTq);
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_swa_persistent(const PrefillArgs &a, double rope_base, void *k_rot,
+                                         bool rope, hipStream_t s) {
+    const int group = a.Hq / a.Hkv;
+    const int n_units = a.B * a.Hkv * (group / kWaves);
+    const int n_tiles = (a.T + kTq - 1) / kTq;
+    const int cus = device_cu_count();
+    // one run per CU: enough runs to cover every CU once, each a contiguous range;
+    // a run's byte span (its tiles plus the window before them) must stay below
+    // 2^31 for the 32-bit offsets
+    int runs_per_unit = std::max(1, std::min(n_tiles, (cus + n_units - 1) / n_units));
+    const int64_t row_bytes = (int64_t)a.Hq * kDqk * 2;
+    const int64_t max_tiles =
+        std::max<int64_t>(1, ((1ll << 31) / row_bytes - 2 * kKb - kSwaMaxWindow) / kTq);
+    runs_per_unit = (int)std::max<int64_t>(runs_per_unit, (n_tiles + max_tiles - 1) / max_tiles);
+    const int tiles_per_run = (n_tiles + runs_per_unit - 1) / runs_per_unit;
+    const int runs = (n_tiles + tiles_per_run - 1) / tiles_per_run;
+    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    const dim3 grid((unsigned)(n_units * runs)), block(kThreads);
+    SwaRope rp{rope_base, (uint16_t *)k_rot};
+    if (rope)
+        prefill_swa_kernel<true><<<grid, block, 0, s>>>(a, rp, n_units, n_tiles, tiles_per_run,
+                                                         scale_log2);
+    else
+        prefill_swa_kernel<false><<<grid, block, 0, s>>>(a, rp, n_units, n_tiles, tiles_per_run,
+                                                          scale_log2);
+    return hipGetLastError();
+}
+
+}  // namespace sinkattn

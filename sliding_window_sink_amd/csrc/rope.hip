@@ -40,12 +40,9 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T *x, int64_t n_tok, int
     const int ntok = (int)min<int64_t>(kTokens, n_tok - tok0);
     for (int idx = threadIdx.x; idx < ntok * half; idx += kThreads) {
         const int tt = idx / half, c = idx % half;
-        const double theta = pow(base, -2.0 * (double)c / (double)rope_dim);
-        const double phi = (double)pos[tok0 + tt] * theta;
-        double sn, cn;
-        sincos(phi, &sn, &cn);
-        cs[tt][c][0] = (float)cn;
-        cs[tt][c][1] = (float)sn;
+        const float2 v = rope_cos_sin(pos[tok0 + tt], rope_inv_freq(base, c, rope_dim));
+        cs[tt][c][0] = v.x;
+        cs[tt][c][1] = v.y;
     }
     __syncthreads();
     const int per_tok = n_heads * half;
@@ -57,9 +54,10 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T *x, int64_t n_tok, int
         const int i0 = style == 0 ? 2 * c : c;
         const int i1 = style == 0 ? 2 * c + 1 : c + half;
         const float x0 = load_f(row + i0), x1 = load_f(row + i1);
-        const float cn = cs[tt][c][0], sn = cs[tt][c][1];
-        store_f(row + i0, x0 * cn - x1 * sn);
-        store_f(row + i1, x0 * sn + x1 * cn);
+        float y0, y1;
+        rope_pair(x0, x1, make_float2(cs[tt][c][0], cs[tt][c][1]), y0, y1);
+        store_f(row + i0, y0);
+        store_f(row + i1, y1);
     }
 }
 

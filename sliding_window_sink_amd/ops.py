@@ -52,6 +52,8 @@ def _bind(lib):
                                  i32),
         "sinkattn_prefill_global": ([p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, p],
                                     i32),
+        "sinkattn_prefill_swa_rope": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32,
+                                       i32, f64, i32, p], i32),
         "sinkattn_decode_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
         "sinkattn_decode": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32, i32,
                              f32, i32, p, sz, i32, p], i32),
@@ -81,7 +83,7 @@ def lib():
 
 
 EXPORTED = ["sinkattn_abi_version", "sinkattn_status_string", "sinkattn_rope_partial",
-            "sinkattn_prefill_swa", "sinkattn_prefill_global", "sinkattn_decode_workspace_bytes",
+            "sinkattn_prefill_swa", "sinkattn_prefill_swa_rope", "sinkattn_prefill_global", "sinkattn_decode_workspace_bytes",
             "sinkattn_decode", "sinkattn_verify", "sinkattn_kv_append"]
 
 
@@ -162,6 +164,26 @@ def _prefill(fn_name, q, k, v, sink, window, scale, out, return_lse):
 def prefill_swa(q, k, v, sink, window: int = 128, scale=None, out=None, return_lse=False):
     """Causal sliding-window prefill: q [B,T,Hq,192], k [B,T,Hkv,192], v [B,T,Hkv,128]."""
     return _prefill("sinkattn_prefill_swa", q, k, v, sink, window, scale, out, return_lse)
+
+
+def prefill_swa_rope(q, k, v, sink, window: int = 128, base: float = 1e4, rope_dim: int = 64,
+                     k_rot=None, scale=None, out=None, return_lse=False):
+    """SWA prefill with partial RoPE fused into the loads (q, k un-rotated and
+    left untouched); k_rot, if given, receives the rotated k."""
+    _dev(q, k, v, sink, out, k_rot)
+    B, T, Hq, dqk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    if k.shape != (B, T, Hkv, dqk) or v.shape[:3] != (B, T, Hkv) or sink.shape != (Hq,):
+        raise SinkAttnError(-2, "q/k/v/sink shapes disagree")
+    if k_rot is not None and (k_rot.shape != k.shape or k_rot.dtype != k.dtype):
+        raise SinkAttnError(-2, "k_rot must match k")
+    o = out if out is not None else torch.empty((B, T, Hq, dv), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib().sinkattn_prefill_swa_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o), _ptr(lse),
+                                           _ptr(k_rot), B, T, Hq, Hkv, dqk, dv, int(window),
+                                           _scale(scale), int(rope_dim), float(base),
+                                           _dtype_code(q), _stream()))
+    return (o, lse) if return_lse else o
 
 
 def prefill_global(q, k, v, sink, scale=None, out=None, return_lse=False):

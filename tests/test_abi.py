@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(ops.EXPORTED) == names
@@ -109,6 +109,21 @@ def test_verify_validation(lib):
     assert verify(nq=5) == UNSUP                  # 5 * 16 columns > 64 on the bf16 path
     assert verify(max_len=20001) == CAP
     assert verify(kind=0, cap=100) == SHAPE       # ring needs a window >= 1 (window=0 here)
+
+
+def test_prefill_swa_rope_validation(lib):
+    f = lib.sinkattn_prefill_swa_rope
+    def call(window=128, rope_dim=64, dtype=1, base=1e4, k_rot=None, Hq=16):
+        return f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], None, k_rot, 1, 64, Hq, 2, 192, 128,
+                 window, 0.0, rope_dim, base, dtype, None)
+    assert call(window=130) == UNSUP
+    assert call(rope_dim=32) == UNSUP
+    assert call(dtype=0) == UNSUP
+    assert call(rope_dim=63) == SHAPE
+    assert call(base=0.0) == SHAPE
+    assert call(window=0) == SHAPE
+    assert call(k_rot=P(FAKE[1].value + 128)) == ALIAS   # k_rot over k
+    assert call(Hq=15) == SHAPE           # Hq % Hkv != 0
 
 
 def test_rope_and_append_validation(lib):

@@ -122,6 +122,31 @@ def test_prefill_sink_stress(sink_val, window):
         assert_close(lse.permute(0, 2, 1), ref_lse, torch.bfloat16, "lse")
 
 
+@pytest.mark.parametrize("T,Hq,Hkv,window", [(300, 16, 2, 128), (777, 8, 1, 128),
+                                              (100, 16, 1, 1), (64, 8, 1, 129)])
+def test_prefill_swa_rope_fused(T, Hq, Hkv, window):
+    """Fused RoPE + SWA prefill equals rope_partial(q), rope_partial(k), then
+    prefill_swa, bit for bit; the rotated k it writes equals rope_partial(k);
+    and it matches the oracle on oracle-rotated inputs."""
+    _print_case("prefill swa rope fused", T, Hq, Hkv, window)
+    q, k, v, sink = synth.prefill_inputs(400 + T, 1, T, Hq, Hkv, torch.bfloat16)
+    qd, kd, vd, sd = (t.to(DEV) for t in (q, k, v, sink))
+    k_rot = torch.empty_like(kd)
+    o_f, lse_f = ops.prefill_swa_rope(qd, kd, vd, sd, window, 1e4, k_rot=k_rot, return_lse=True)
+    assert torch.equal(qd.cpu(), q) and torch.equal(kd.cpu(), k), "inputs must stay untouched"
+    pos = synth.positions(1, T).to(DEV)
+    qr, kr = qd.clone(), kd.clone()
+    ops.rope_partial(qr, pos, 1e4)
+    ops.rope_partial(kr, pos, 1e4)
+    o_u, lse_u = ops.prefill_swa(qr, kr, vd, sd, window=window, return_lse=True)
+    assert torch.equal(k_rot, kr)
+    assert torch.equal(o_f, o_u) and torch.equal(lse_f, lse_u)
+    qo = oracle.rope_partial(q[0], np.arange(T), 1e4)[None]
+    ko = oracle.rope_partial(k[0], np.arange(T), 1e4)[None]
+    ref_o, _ = oracle.prefill(qo, ko, v, sink, window)
+    assert_close(o_f, ref_o, torch.bfloat16, "fused rope prefill")
+
+
 def test_prefill_zero_query_closed_form():
     """q = 0 makes every visible weight 1/(e^sink + |J|): a wrong window count
     or KV group shows up even in bf16."""
