@@ -1,34 +1,39 @@
-// prefill.hip -- causal sink-attention prefill on gfx950 (bf16 in, fp32 accumulate).
+// prefill.hip -- causal sink-attention prefill on gfx950 (bf16 in, fp32 accumulate):
+// global-attention layers, and sliding windows wider than the persistent SWA
+// kernel holds (W > 129).
 //
 // Computes, for every query token i of a sequence and every query head h
 // (MiMo-V2-Flash Technical Report, Section 2.2, equations 1-4):
 //   a_ij = q_i . k_j * scale,  m_i = max(max_j a_ij, sink_h),
 //   o_i  = sum_j exp(a_ij - m_i) v_j / (exp(sink_h - m_i) + sum_j exp(a_ij - m_i))
-// over the visible keys j <= i (and i - j < W for a sliding-window layer).
+// over the visible keys j <= i (and i - j < W for a windowed layer).
 //
 // The softmax is evaluated online, flash style, with the running state seeded
 // by the sink: m <- sink, l <- 1 (l <- 0 when sink = -inf), acc <- 0.  That makes
 // the sink term exact and counted once, with no extra pass.
 //
 // Work decomposition (one workgroup = 8 waves):
-//   - a workgroup owns one KV group g (Table 1: 8 query heads per KV head for
-//     SWA layers, 16 for global layers, handled as two workgroups of 8) and a
-//     tile of 32 consecutive query tokens; wave w owns query head 8*part + w;
+//   - a workgroup owns one KV group g (Table 1: 16 query heads per KV head for
+//     global layers, handled as two workgroups of 8) and a tile of 32
+//     consecutive query tokens; wave w owns query head 8*part + w;
 //   - the 32 tokens are the 32 MFMA columns; Q stays in registers for the
 //     whole tile (12 k-steps of 16 dims);
-//   - keys stream through LDS in blocks of 32, double buffered: every K/V
-//     block is fetched from memory once per workgroup and read by all 8 heads;
+//   - keys stream in blocks of 32 through two LDS stages; every block is
+//     fetched once per workgroup and read by all 8 heads; the global loads of
+//     block j+2 are issued while block j is computed (two register sets), so
+//     about two blocks of compute cover the memory latency;
 //   - scores are computed transposed, S^T = K Q^T (rows = keys, columns =
 //     queries), so each lane owns one query column and the row max / sum are
 //     per-lane register reductions plus one exchange between wave halves;
 //   - K rows are written into LDS in the order that makes C-register i of lane
 //     half hh hold key 16*hh + i, so P^T feeds the PV MFMA directly as its B
-//     operand and V is stored transposed ([dim][key]) so its A operand is one
+//     operand, and V is stored transposed ([dim][key]) so its A operand is one
 //     16-byte LDS read per lane.
+// Global memory is read through raw buffer descriptors (rows past the end of
+// the sequence read as zero; stores past it are dropped).
 // Workgroup order: blockIdx % units picks (batch, KV group, head half), so on
-// the 8 XCDs of MI355X each XCD sees consecutive tiles of the same KV group and
-// the overlapping K/V windows hit in its L2.  Global layers run the longest
-// (last) tiles first.
+// the 8 XCDs of MI355X each XCD sees tiles of the same KV group and the shared
+// K/V blocks hit in its L2.  Global layers run the longest (last) tiles first.
 #include "common.h"
 
 namespace sinkattn {
@@ -49,14 +54,23 @@ struct PrefillSmem {
     uint16_t vt[2][kDv * kVPitch];
 };
 
+// V^T LDS row holding output dim d: the PV accumulator block db, C-row
+// rho = 8a + 4hh + e holds dim 32a + 16(db/2) + 8hh + 4(db%2) + e, so a lane owns
+// runs of 8 consecutive output dims (16-byte stores).
+__device__ __forceinline__ int pv_row_of_dim(int d) {
+    const int a = d >> 5, j = (d >> 4) & 1, hh = (d >> 3) & 1, dbl = (d >> 2) & 1, e = d & 3;
+    return 32 * (2 * j + dbl) + 8 * a + 4 * hh + e;
+}
+
+struct Staged {
+    uint4 k[2];
+    uint4 v;
+};
+
 template <bool kWindowed>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, int n_units,
                                                                  int n_tiles, float scale_log2) {
     __shared__ PrefillSmem sm;
-    const uint16_t *__restrict__ q = (const uint16_t *)a.q;
-    const uint16_t *__restrict__ k = (const uint16_t *)a.k;
-    const uint16_t *__restrict__ v = (const uint16_t *)a.v;
-    uint16_t *__restrict__ o = (uint16_t *)a.o;
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, window = a.window;
     const int group = Hq / Hkv;
     const int parts = group / kWaves;
@@ -74,16 +88,22 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
     const int t0 = tile * kTq;
     const int query = t0 + r;  // this lane's query column
 
+    const size_t row0 = (size_t)b * T;
+    const uint32_t qrow = (uint32_t)Hq * kDqk * 2, orow = (uint32_t)Hq * kDv * 2;
+    const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
+    const BufRsrc qbuf = make_buf((const uint16_t *)a.q + row0 * Hq * kDqk, (uint64_t)T * qrow);
+    const BufRsrc kbuf = make_buf((const uint16_t *)a.k + row0 * Hkv * kDqk, (uint64_t)T * krow);
+    const BufRsrc vbuf = make_buf((const uint16_t *)a.v + row0 * Hkv * kDv, (uint64_t)T * vrow);
+    const BufRsrc obuf = make_buf((uint16_t *)a.o + row0 * Hq * kDv, (uint64_t)T * orow);
+    const uint32_t kcol = (uint32_t)g * kDqk * 2, vcol = (uint32_t)g * kDv * 2;
+
     // Q^T as the B operand: k-step s, lane half hh -> head dims (2s+hh)*8 .. +7.
-    bf16x8 qf[kDqk / 16];
+    uint4 qf[kDqk / 16];
     {
-        const bool ok = query < T;
-        const uint16_t *qrow = q + ((size_t)(b * T + (ok ? query : 0)) * Hq + h) * kDqk;
+        const uint32_t off = (uint32_t)query * qrow + (uint32_t)h * kDqk * 2 + (uint32_t)hh * 16;
 #pragma unroll
-        for (int s = 0; s < kDqk / 16; ++s) {
-            uint4 u = ok ? *(const uint4 *)(qrow + (2 * s + hh) * 8) : make_uint4(0, 0, 0, 0);
-            qf[s] = as_bf16x8(u);
-        }
+        for (int s = 0; s < kDqk / 16; ++s)
+            qf[s] = buf_load16(qbuf, off + (uint32_t)s * 32);
     }
 
     const int kstart = kWindowed ? max(0, t0 - window + 1) : 0;
@@ -91,42 +111,36 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
     const int kb0 = kstart & ~(kKb - 1);
     const int nblk = (kend - kb0 + kKb - 1) / kKb;
 
-    const size_t krow_stride = (size_t)Hkv * kDqk;
-    const size_t vrow_stride = (size_t)Hkv * kDv;
-    const uint16_t *kbase = k + (size_t)b * T * krow_stride + (size_t)g * kDqk;
-    const uint16_t *vbase = v + (size_t)b * T * vrow_stride + (size_t)g * kDv;
+    // Per-thread staging offsets, computed once: K pieces c = tid, tid + 512 (key c/24,
+    // dims (c%24)*8..+7); V piece tid (key tid/16, dims (tid%16)*8..+7).  Output dim
+    // 8*dc + j sits in V^T row vrow0 + 32*(j/4) + j%4 (see pv_row_of_dim).
+    const bool k2 = tid + kThreads < kKChunks;  // wave-uniform
+    uint32_t kg_off[2];
+    int kl_off[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = min(tid + u * kThreads, kKChunks - 1);
+        kg_off[u] = (uint32_t)(c / (kDqk / 8)) * krow + kcol + (uint32_t)(c % (kDqk / 8)) * 16;
+        kl_off[u] = row_of_key(c / (kDqk / 8)) * kKPitch + (c % (kDqk / 8)) * 8;
+    }
+    const uint32_t vg_off = (uint32_t)(tid / (kDv / 8)) * vrow + vcol + (uint32_t)(tid % (kDv / 8)) * 16;
+    const int vl_off = pv_row_of_dim((tid % (kDv / 8)) * 8) * kVPitch + tid / (kDv / 8);
 
-    auto load_block = [&](int kb, uint4 (&kreg)[2], uint4 &vreg) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int c = tid + u * kThreads;
-            kreg[u] = make_uint4(0, 0, 0, 0);
-            if (c < kKChunks) {
-                const int kk = c / (kDqk / 8), d = c % (kDqk / 8);
-                const int key = kb + kk;
-                if (key < T)
-                    kreg[u] = *(const uint4 *)(kbase + (size_t)key * krow_stride + d * 8);
-            }
-        }
-        const int kk = tid / (kDv / 8), dc = tid % (kDv / 8);
-        const int key = kb + kk;
-        vreg = key < T ? *(const uint4 *)(vbase + (size_t)key * vrow_stride + dc * 8)
-                       : make_uint4(0, 0, 0, 0);
+    auto load_block = [&](int kb, Staged &st) {
+        st.k[0] = buf_load16(kbuf, (uint32_t)kb * krow + kg_off[0]);
+        if (k2)
+            st.k[1] = buf_load16(kbuf, (uint32_t)kb * krow + kg_off[1]);
+        st.v = buf_load16(vbuf, (uint32_t)kb * vrow + vg_off);
     };
-    auto store_block = [&](int buf, const uint4 (&kreg)[2], const uint4 &vreg) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int c = tid + u * kThreads;
-            if (c < kKChunks) {
-                const int kk = c / (kDqk / 8), d = c % (kDqk / 8);
-                *(uint4 *)&sm.k[buf][row_of_key(kk) * kKPitch + d * 8] = kreg[u];
-            }
-        }
-        const int kk = tid / (kDv / 8), dc = tid % (kDv / 8);
-        const uint32_t w[4] = {vreg.x, vreg.y, vreg.z, vreg.w};
+    auto store_block = [&](int buf, const Staged &st) {
+        *(uint4 *)&sm.k[buf][kl_off[0]] = st.k[0];
+        if (k2)
+            *(uint4 *)&sm.k[buf][kl_off[1]] = st.k[1];
+        const uint32_t w[4] = {st.v.x, st.v.y, st.v.z, st.v.w};
+        uint16_t *vt = &sm.vt[buf][vl_off];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            sm.vt[buf][(dc * 8 + j) * kVPitch + kk] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+            vt[(32 * (j >> 2) + (j & 3)) * kVPitch] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
     };
 
     // Online-softmax state in log2 units, seeded with the sink.
@@ -138,19 +152,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
     for (int db = 0; db < 4; ++db)
         acc[db] = f32x16{};
 
-    {
-        uint4 kreg[2], vreg;
-        load_block(kb0, kreg, vreg);
-        store_block(0, kreg, vreg);
-    }
+    // pipeline: block j computed from LDS stage j&1; block j+1 stored at the end of
+    // block j from register set (j+1)&1; block j+2 loaded at the start of block j.
+    // The loop is unrolled by two so the two register sets are named statically
+    // (a runtime-indexed register array would live in scratch memory).
+    Staged st0, st1;
+    load_block(kb0, st0);
+    if (nblk > 1)
+        load_block(kb0 + kKb, st1);
+    store_block(0, st0);
     __syncthreads();
 
-    for (int j = 0; j < nblk; ++j) {
+    auto step = [&](int j, Staged &cur_next2, Staged &next1) {
+        // cur_next2: the set that held block j, refilled with block j+2;
+        // next1: the set holding block j+1, stored into LDS at the end.
         const int kb = kb0 + j * kKb;
-        const bool more = j + 1 < nblk;
-        uint4 kreg[2], vreg;
-        if (more)
-            load_block(kb + kKb, kreg, vreg);
+        if (j + 2 < nblk)
+            load_block(kb + 2 * kKb, cur_next2);
         const uint16_t *ks = sm.k[j & 1];
         const uint16_t *vs = sm.vt[j & 1];
 
@@ -158,46 +176,42 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
         f32x16 sc = f32x16{};
 #pragma unroll
         for (int s = 0; s < kDqk / 16; ++s) {
-            const uint4 ka = *(const uint4 *)(ks + r * kKPitch + (2 * s + hh) * 8);
-            sc = mfma32x32x16(as_bf16x8(ka), qf[s], sc);
+            const bf16x8 ka = as_bf16x8(*(const uint4 *)(ks + r * kKPitch + (2 * s + hh) * 8));
+            sc = mfma32x32x16(ka, as_bf16x8(qf[s]), sc);
         }
 
         const bool full = (kb + kKb - 1 <= t0) && (!kWindowed || (t0 + kTq - 1 - kb < window));
-        float x[16];
         float bm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float val = sc[i] * scale_log2;
             if (!full) {
                 const int key = kb + 16 * hh + i;
                 const bool vis = key <= query && (!kWindowed || query - key < window);
-                val = vis ? val : -INFINITY;
+                sc[i] = vis ? sc[i] : -INFINITY;
             }
-            x[i] = val;
-            bm = fmaxf(bm, val);
+            bm = fmaxf(bm, sc[i]);
         }
-        bm = max_across_halves(bm);
-        const float mn = fmaxf(m, bm);
-        const float mu = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = fast_exp2(m - mu);
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            x[i] = fast_exp2(x[i] - mu);
-            ps += x[i];
-        }
-        l = l * alpha + ps;
+        bm = max_across_halves(bm) * scale_log2;
+        // raise m only when the block max passes it by more than the slack
+        const bool up = bm > m + kRescaleSlack || (m == -INFINITY && bm > -INFINITY);
+        const float mn = up ? bm : m;
+        const float alpha = up ? fast_exp2(m - mn) : 1.f;
         m = mn;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-            acc[db] *= alpha;
-
+        const float mu = (mn == -INFINITY) ? 0.f : mn;
+        float ps = 0.f;
         bf16x8 pb[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < 16; ++i) {
+            const float p = fast_exp2(__fmaf_rn(sc[i], scale_log2, -mu));
+            ps += p;
+            pb[i >> 3][i & 7] = (__bf16)p;
+        }
+        l = __fmaf_rn(l, alpha, ps);
+        if (__builtin_amdgcn_ballot_w64(up) != 0) {  // wave-uniform rescale
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pb[t][e] = (__bf16)x[8 * t + e];
+            for (int db = 0; db < 4; ++db)
+                acc[db] *= alpha;
+        }
 
         // O^T += V^T P^T: A = V^T rows (dims) from LDS, B = P^T from registers.
 #pragma unroll
@@ -208,29 +222,35 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
                 acc[db] = mfma32x32x16(as_bf16x8(va), pb[t], acc[db]);
             }
 
-        if (more)
-            store_block((j + 1) & 1, kreg, vreg);
+        if (j + 1 < nblk)
+            store_block((j + 1) & 1, next1);
         __syncthreads();
+    };
+    for (int j = 0; j < nblk; j += 2) {
+        step(j, st0, st1);
+        if (j + 1 < nblk)
+            step(j + 1, st1, st0);
     }
 
     // Epilogue: o = acc / l, with l summed over both wave halves.
     const float lt = sum_across_halves(l);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (query < T) {
-        uint16_t *orow = o + ((size_t)(b * T + query) * Hq + h) * kDv;
+    const uint32_t obase = (uint32_t)query * orow + (uint32_t)h * kDv * 2 + (uint32_t)hh * 16;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+    for (int aa = 0; aa < 4; ++aa)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                uint2 w;
-                w.x = pack_bf16x2(acc[db][4 * i4 + 0] * inv, acc[db][4 * i4 + 1] * inv);
-                w.y = pack_bf16x2(acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv);
-                *(uint2 *)(orow + 32 * db + 8 * i4 + 4 * hh) = w;
-            }
-        if (a.lse && hh == 0) {
-            const float mu = (m == -INFINITY) ? 0.f : m;
-            a.lse[((size_t)b * Hq + h) * T + query] = lt > 0.f ? (mu + log2f(lt)) * kLn2 : -INFINITY;
+        for (int jj = 0; jj < 2; ++jj) {
+            const f32x16 &lo = acc[2 * jj], &hi = acc[2 * jj + 1];
+            uint4 w;
+            w.x = pack_bf16x2(lo[4 * aa + 0] * inv, lo[4 * aa + 1] * inv);
+            w.y = pack_bf16x2(lo[4 * aa + 2] * inv, lo[4 * aa + 3] * inv);
+            w.z = pack_bf16x2(hi[4 * aa + 0] * inv, hi[4 * aa + 1] * inv);
+            w.w = pack_bf16x2(hi[4 * aa + 2] * inv, hi[4 * aa + 3] * inv);
+            buf_store16(obuf, obase + (uint32_t)(64 * aa + 32 * jj), w);
         }
+    if (a.lse && hh == 0 && query < T) {
+        const float mu = (m == -INFINITY) ? 0.f : m;
+        a.lse[((size_t)b * Hq + h) * T + query] = lt > 0.f ? (mu + log2f(lt)) * kLn2 : -INFINITY;
     }
 }
 

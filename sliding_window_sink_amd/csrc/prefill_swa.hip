@@ -135,17 +135,29 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
     };
 
     // ---- key blocks: global -> registers -> (rotate) -> LDS ring slot ----
+    // Per-thread offsets, computed once: K pieces c = tid, tid + 512 (key c/24, dims
+    // (c%24)*8..+7); V piece tid (key tid/16, dims (tid%16)*8..+7).  Output dim
+    // 8*dc + j sits in V^T row vrow0 + 32*(j/4) + j%4 (see pv_row_of_dim).
+    const bool k2 = tid + kThreads < kKChunks;  // wave-uniform
+    uint32_t kg_off[2];
+    int kl_off[2], k_key[2], k_d[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = min(tid + u * kThreads, kKChunks - 1);
+        k_key[u] = c / (kDqk / 8);
+        k_d[u] = c % (kDqk / 8);
+        kg_off[u] = (uint32_t)k_key[u] * krow + kcol + (uint32_t)k_d[u] * 16;
+        kl_off[u] = row_of_key(k_key[u]) * kKPitch + k_d[u] * 8;
+    }
+    const uint32_t vg_off = (uint32_t)(tid / (kDv / 8)) * vrow + vcol + (uint32_t)(tid % (kDv / 8)) * 16;
+    const int vl_off = pv_row_of_dim((tid % (kDv / 8)) * 8) * kVPitch + tid / (kDv / 8);
+
     auto load_block = [&](int jb, uint4 (&kreg)[2], uint4 &vreg) {
         const uint32_t rel = (uint32_t)(jb * kKb - tbase);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int c = tid + u * kThreads;
-            if (u == 0 || c < kKChunks)  // wave-uniform: waves 0..3 take a second piece
-                kreg[u] = buf_load16(kbuf, (rel + c / (kDqk / 8)) * krow + kcol +
-                                               (uint32_t)(c % (kDqk / 8)) * 16);
-        }
-        vreg = buf_load16(vbuf, (rel + tid / (kDv / 8)) * vrow + vcol +
-                                    (uint32_t)(tid % (kDv / 8)) * 16);
+        kreg[0] = buf_load16(kbuf, rel * krow + kg_off[0]);
+        if (k2)
+            kreg[1] = buf_load16(kbuf, rel * krow + kg_off[1]);
+        vreg = buf_load16(vbuf, rel * vrow + vg_off);
     };
     // cs_buf: hi_rot buffer of the block's tokens (rope only); own: this run writes k_rot
     auto store_block = [&](int jb, const uint4 (&kreg)[2], const uint4 &vreg, int cs_buf,
@@ -154,26 +166,23 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
         const uint32_t rel = (uint32_t)(jb * kKb - tbase);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int c = tid + u * kThreads;
-            if (u == 0 || c < kKChunks) {
-                const int kk = c / (kDqk / 8), d = c % (kDqk / 8);
+            if (u == 0 || k2) {
                 uint4 x = kreg[u];
-                if (kRope && d < 8) {
+                if (kRope && k_d[u] < 8) {
                     float2 cs[4];
-                    rot4(cs_buf, kk, 4 * d, cs);
+                    rot4(cs_buf, k_key[u], 4 * k_d[u], cs);
                     x = rope_chunk_bf16(x, cs);
                 }
-                *(uint4 *)&sm.k[slot][row_of_key(kk) * kKPitch + d * 8] = x;
+                *(uint4 *)&sm.k[slot][kl_off[u]] = x;
                 if (kRope && write_krot && own)
-                    buf_store16(krbuf, (rel + kk) * krow + kcol + (uint32_t)d * 16, x);
+                    buf_store16(krbuf, rel * krow + kg_off[u], x);
             }
         }
-        const int kk = tid / (kDv / 8), dc = tid % (kDv / 8);
         const uint32_t w[4] = {vreg.x, vreg.y, vreg.z, vreg.w};
+        uint16_t *vt = &sm.vt[slot][vl_off];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            sm.vt[slot][pv_row_of_dim(dc * 8 + j) * kVPitch + kk] =
-                (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+            vt[(32 * (j >> 2) + (j & 3)) * kVPitch] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
     };
     // Q^T operand of one tile: k-step s, half hh -> dims (2s+hh)*8 .. +7 of token t0+r.
     auto load_q = [&](int t0, uint4 (&qr)[kDqk / 16]) {
