@@ -102,6 +102,17 @@ __host__ __device__ __forceinline__ int key_of_row(int r) {
     return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
 }
 
+// Which (key, 8-dim chunk) of a 32-key x 128-dim V block thread tid (of 512)
+// stages.  Each wave takes 16 keys x 4 chunks, the chunks chosen so that the
+// scattered 2-byte writes into the transposed V^T tile (rows pv_row_of_dim,
+// 80-byte pitch) land in 32 distinct LDS banks; the plain 4-keys x 16-chunks
+// order aliased them 4-way.
+__device__ __forceinline__ void v_stage_coords(int tid, int &kk, int &dc) {
+    const int wave = tid >> 6, lane = tid & 63, s = wave >> 1, idx = lane >> 4;
+    kk = (lane & 15) + 16 * (wave & 1);
+    dc = (s & 1) * 2 + (s >> 1) * 8 + (idx & 1) + (idx >> 1) * 4;
+}
+
 // ---- partial RoPE (shared by the standalone kernel and the fused prefill) ----
 // theta_c = base^(-2c/rope_dim), angle = pos * theta_c, both in fp64 (an fp32
 // angle is off by ~1e-3 rad near position 1e5); cos/sin rounded to fp32.

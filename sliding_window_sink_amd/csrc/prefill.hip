@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
     const int nblk = (kend - kb0 + kKb - 1) / kKb;
 
     // Per-thread staging offsets, computed once: K pieces c = tid, tid + 512 (key c/24,
-    // dims (c%24)*8..+7); V piece tid (key tid/16, dims (tid%16)*8..+7).  Output dim
+    // dims (c%24)*8..+7); V piece of v_stage_coords.  Output dim
     // 8*dc + j sits in V^T row vrow0 + 32*(j/4) + j%4 (see pv_row_of_dim).
     const bool k2 = tid + kThreads < kKChunks;  // wave-uniform
     uint32_t kg_off[2];
@@ -123,8 +123,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
         kg_off[u] = (uint32_t)(c / (kDqk / 8)) * krow + kcol + (uint32_t)(c % (kDqk / 8)) * 16;
         kl_off[u] = row_of_key(c / (kDqk / 8)) * kKPitch + (c % (kDqk / 8)) * 8;
     }
-    const uint32_t vg_off = (uint32_t)(tid / (kDv / 8)) * vrow + vcol + (uint32_t)(tid % (kDv / 8)) * 16;
-    const int vl_off = pv_row_of_dim((tid % (kDv / 8)) * 8) * kVPitch + tid / (kDv / 8);
+    int v_kk, v_dc;
+    v_stage_coords(tid, v_kk, v_dc);
+    const uint32_t vg_off = (uint32_t)v_kk * vrow + vcol + (uint32_t)v_dc * 16;
+    const int vl_off = pv_row_of_dim(v_dc * 8) * kVPitch + v_kk;
 
     auto load_block = [&](int kb, Staged &st) {
         st.k[0] = buf_load16(kbuf, (uint32_t)kb * krow + kg_off[0]);
@@ -180,17 +182,21 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
             sc = mfma32x32x16(ka, as_bf16x8(qf[s]), sc);
         }
 
+        // Only blocks on the causal diagonal or the window edge need the per-element
+        // mask; the test is uniform, so the mask sits behind a scalar branch.
         const bool full = (kb + kKb - 1 <= t0) && (!kWindowed || (t0 + kTq - 1 - kb < window));
-        float bm = -INFINITY;
+        if (!full) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (!full) {
+            for (int i = 0; i < 16; ++i) {
                 const int key = kb + 16 * hh + i;
                 const bool vis = key <= query && (!kWindowed || query - key < window);
                 sc[i] = vis ? sc[i] : -INFINITY;
             }
-            bm = fmaxf(bm, sc[i]);
         }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            bm = fmaxf(bm, sc[i]);
         bm = max_across_halves(bm) * scale_log2;
         // raise m only when the block max passes it by more than the slack
         const bool up = bm > m + kRescaleSlack || (m == -INFINITY && bm > -INFINITY);

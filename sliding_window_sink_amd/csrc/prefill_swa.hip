@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
 
     // ---- key blocks: global -> registers -> (rotate) -> LDS ring slot ----
     // Per-thread offsets, computed once: K pieces c = tid, tid + 512 (key c/24, dims
-    // (c%24)*8..+7); V piece tid (key tid/16, dims (tid%16)*8..+7).  Output dim
+    // (c%24)*8..+7); V piece of v_stage_coords.  Output dim
     // 8*dc + j sits in V^T row vrow0 + 32*(j/4) + j%4 (see pv_row_of_dim).
     const bool k2 = tid + kThreads < kKChunks;  // wave-uniform
     uint32_t kg_off[2];
@@ -149,8 +149,10 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
         kg_off[u] = (uint32_t)k_key[u] * krow + kcol + (uint32_t)k_d[u] * 16;
         kl_off[u] = row_of_key(k_key[u]) * kKPitch + k_d[u] * 8;
     }
-    const uint32_t vg_off = (uint32_t)(tid / (kDv / 8)) * vrow + vcol + (uint32_t)(tid % (kDv / 8)) * 16;
-    const int vl_off = pv_row_of_dim((tid % (kDv / 8)) * 8) * kVPitch + tid / (kDv / 8);
+    int v_kk, v_dc;
+    v_stage_coords(tid, v_kk, v_dc);
+    const uint32_t vg_off = (uint32_t)v_kk * vrow + vcol + (uint32_t)v_dc * 16;
+    const int vl_off = pv_row_of_dim(v_dc * 8) * kVPitch + v_kk;
 
     auto load_block = [&](int jb, uint4 (&kreg)[2], uint4 &vreg) {
         const uint32_t rel = (uint32_t)(jb * kKb - tbase);
@@ -268,16 +270,20 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
             }
             // raw scores; masked ones -> -inf.  scale_log2 > 0, so the max of the raw
             // scores times the scale is the max of the scaled logits.
+            // only the window-edge and diagonal blocks need the per-element mask;
+            // the test is uniform, so the mask sits behind a scalar branch
             const bool full = (kb + kKb - 1 <= t0) && (t0 + kTq - 1 - kb < window);
-            float bm = -INFINITY;
+            if (!full) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (!full) {
+                for (int i = 0; i < 16; ++i) {
                     const int key = kb + 16 * hh + i;
                     sc[i] = (key <= query && query - key < window) ? sc[i] : -INFINITY;
                 }
-                bm = fmaxf(bm, sc[i]);
             }
+            float bm = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                bm = fmaxf(bm, sc[i]);
             bm = max_across_halves(bm) * scale_log2;
             // raise m only when the block max passes it by more than the slack
             const bool up = bm > m + kRescaleSlack || (m == -INFINITY && bm > -INFINITY);
