@@ -14,21 +14,25 @@
 //
 // Decomposition: one workgroup (4 waves) per (sequence, KV group, context
 // chunk).  Columns of the 32x32 MFMA tile are (token, head) pairs of the KV
-// group: nq*group <= 64, so one or two column blocks.  The chunk's keys are cut
-// into blocks of 32 that the 4 waves take in turn; each wave keeps its own
-// online-softmax state (no sink), then the 4 states are merged through LDS.
-// With one chunk the merge adds the sink and writes o; with several it writes
-// the unnormalised (m, l, acc) of the chunk to the workspace and a combine
-// kernel adds the sink exactly once:
+// group: nq*group <= 64, so one or two column blocks.  The chunk's cached keys
+// are cut into blocks of 32 that the 4 waves take in turn (the <= 8 new tokens
+// form one extra block at the end); each wave keeps its own online-softmax
+// state (no sink), then the 4 states are merged through LDS.  With one chunk
+// the merge adds the sink and writes o; with several it writes the
+// unnormalised (m, l, acc) of the chunk to the workspace and a combine kernel
+// adds the sink exactly once:
 //   M = max(sink, max_c m_c),  Z = e^(sink-M) + sum_c l_c e^(m_c-M),
 //   o = sum_c acc_c e^(m_c-M) / Z.
 //
-// Memory access: K and V are loaded straight from HBM into MFMA operand
-// registers (no LDS round trip; every byte is read once).  For K the lane that
-// owns A-row r reads 32 contiguous bytes of that key per k-step.  For V the
-// output-dim order is chosen as dim = 4*row + block, so each lane reads 8
-// contiguous bytes (4 dims) of 16 keys and two lanes cover a 256-byte row:
-// fully coalesced; a register shuffle then builds the V^T operands.
+// Memory access: decode is HBM bound (16 FLOP per byte at 16 heads per KV
+// head), so K and V go straight from HBM into MFMA operand registers (every
+// byte read once, no LDS round trip) through raw buffer descriptors (keys past
+// the valid range read as zero without a branch).  Each wave double-buffers:
+// the loads of its next block are in flight while it computes the current one.
+// For K the lane that owns A-row r reads 32 contiguous bytes of that key per
+// k-step.  For V the output-dim order is chosen as dim = 4*row + block, so each
+// lane reads 8 contiguous bytes (4 dims) of 16 keys and two lanes cover a
+// 256-byte row; a register shuffle then builds the V^T operands.
 #include "common.h"
 
 namespace sinkattn {
@@ -38,6 +42,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKb = 32;
 constexpr int kMergeStride = kDv + 4;  // floats per (wave, column): acc[128], m, l, pad
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every descriptor: reads 0
 
 struct CachedGeom {
     int b, g, group, P, lo, hi, rlo, rhi;
@@ -60,19 +65,11 @@ __device__ __forceinline__ CachedGeom cached_geom(const CachedArgs &a, int split
     return c;
 }
 
-// Row of key position p in the cache or in the new-token tensor (nullptr if p is
-// outside [rlo, rhi)).
-__device__ __forceinline__ const uint16_t *key_row(const CachedArgs &a, const CachedGeom &c, int p,
-                                                   const uint16_t *cache, const uint16_t *fresh,
-                                                   int d) {
-    if (p < c.rlo || p >= c.rhi)
-        return nullptr;
-    if (p < c.P) {
-        const int slot = a.ring ? (p % a.cap) : p;
-        return cache + (((size_t)c.b * a.Hkv + c.g) * a.cap + slot) * d;
-    }
-    return fresh + (((size_t)c.b * a.nq + (p - c.P)) * a.Hkv + c.g) * d;
-}
+// One block of 32 keys in MFMA operand layout.
+struct KVRegs {
+    uint4 k[kDqk / 16];  // A-row r = key key_of_row(r); k-step s: dims (2s+hh)*8 .. +7
+    uint2 v[16];         // keys 16*hh + i, dims 4r .. 4r+3
+};
 
 template <int NCB>
 __global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, float scale_log2) {
@@ -83,43 +80,51 @@ __global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, flo
     const CachedGeom c = cached_geom(a, split, blockIdx.x / a.n_splits);
     const int group = c.group;
     const int n_cols = a.nq * group;
+    const int Hkv = a.Hkv, nq = a.nq;
 
-    const uint16_t *kc = (const uint16_t *)a.k_cache;
-    const uint16_t *vc = (const uint16_t *)a.v_cache;
-    const uint16_t *kn = (const uint16_t *)a.k_new;
-    const uint16_t *vn = (const uint16_t *)a.v_new;
+    // Descriptors: this (sequence, KV head)'s cache rows, and the new tokens.
+    const size_t crow0 = ((size_t)c.b * Hkv + c.g) * a.cap;
+    const uint64_t cache_rows = a.ring ? (uint64_t)a.cap : (uint64_t)c.P;
+    const BufRsrc kc = make_buf((const uint16_t *)a.k_cache + crow0 * kDqk, cache_rows * kDqk * 2);
+    const BufRsrc vc = make_buf((const uint16_t *)a.v_cache + crow0 * kDv, cache_rows * kDv * 2);
+    const size_t nrow0 = (size_t)c.b * nq * Hkv + c.g;  // row of token t: nrow0 + t*Hkv
+    const uint64_t new_bytes_k = ((uint64_t)(nq - 1) * Hkv + 1) * kDqk * 2;
+    const uint64_t new_bytes_v = ((uint64_t)(nq - 1) * Hkv + 1) * kDv * 2;
+    const BufRsrc kn = make_buf((const uint16_t *)a.k_new + nrow0 * kDqk, new_bytes_k);
+    const BufRsrc vn = make_buf((const uint16_t *)a.v_new + nrow0 * kDv, new_bytes_v);
 
     // Decode: store the new token into the cache (slot / index P).  Nothing in
     // this launch reads that cache row.
-    if (a.write_new && split == 0) {
+    if (a.write_new && split == 0 && (a.ring || c.P < a.cap)) {
         const int slot = a.ring ? (c.P % a.cap) : c.P;
-        if (a.ring || c.P < a.cap) {
-            uint16_t *kd = (uint16_t *)a.k_cache + (((size_t)c.b * a.Hkv + c.g) * a.cap + slot) * kDqk;
-            uint16_t *vd = (uint16_t *)a.v_cache + (((size_t)c.b * a.Hkv + c.g) * a.cap + slot) * kDv;
-            const uint16_t *ks = kn + ((size_t)c.b * a.nq * a.Hkv + c.g) * kDqk;
-            const uint16_t *vs = vn + ((size_t)c.b * a.nq * a.Hkv + c.g) * kDv;
-            if (tid < kDqk / 8)
-                *(uint4 *)(kd + tid * 8) = *(const uint4 *)(ks + tid * 8);
-            else if (tid < kDqk / 8 + kDv / 8)
-                *(uint4 *)(vd + (tid - kDqk / 8) * 8) = *(const uint4 *)(vs + (tid - kDqk / 8) * 8);
-        }
+        uint16_t *kd = (uint16_t *)a.k_cache + (crow0 + slot) * kDqk;
+        uint16_t *vd = (uint16_t *)a.v_cache + (crow0 + slot) * kDv;
+        const uint16_t *ks = (const uint16_t *)a.k_new + nrow0 * kDqk;
+        const uint16_t *vs = (const uint16_t *)a.v_new + nrow0 * kDv;
+        if (tid < kDqk / 8)
+            *(uint4 *)(kd + tid * 8) = *(const uint4 *)(ks + tid * 8);
+        else if (tid < kDqk / 8 + kDv / 8)
+            *(uint4 *)(vd + (tid - kDqk / 8) * 8) = *(const uint4 *)(vs + (tid - kDqk / 8) * 8);
     }
 
     // Q^T operands; column cb*32 + r is (token t, head) = divmod(column, group).
     bf16x8 qf[NCB][kDqk / 16];
     int qpos[NCB];
+    {
+        const BufRsrc qb = make_buf((const uint16_t *)a.q + (size_t)c.b * nq * a.Hq * kDqk,
+                                    (uint64_t)nq * a.Hq * kDqk * 2);
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        const int col = cb * 32 + r;
-        const bool ok = col < n_cols;
-        const int t = ok ? col / group : 0;
-        const int h = c.g * group + (ok ? col % group : 0);
-        qpos[cb] = ok ? c.P + t : -1;
-        const uint16_t *qrow = (const uint16_t *)a.q + (((size_t)c.b * a.nq + t) * a.Hq + h) * kDqk;
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int col = cb * 32 + r;
+            const bool ok = col < n_cols;
+            const int t = col / group;
+            qpos[cb] = ok ? c.P + t : -1;
+            const uint32_t off = ok ? ((uint32_t)(t * a.Hq + c.g * group + col % group) * kDqk +
+                                       (uint32_t)hh * 8) * 2
+                                    : kOob;
 #pragma unroll
-        for (int s = 0; s < kDqk / 16; ++s) {
-            uint4 u = ok ? *(const uint4 *)(qrow + (2 * s + hh) * 8) : make_uint4(0, 0, 0, 0);
-            qf[cb][s] = as_bf16x8(u);
+            for (int s = 0; s < kDqk / 16; ++s)
+                qf[cb][s] = as_bf16x8(buf_load16(qb, off + (uint32_t)s * 32));
         }
     }
 
@@ -134,28 +139,50 @@ __global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, flo
             acc[cb][db] = f32x16{};
     }
 
-    const int nkeys = max(0, c.rhi - c.rlo);
-    const int nblk = (nkeys + kKb - 1) / kKb;
+    // Blocks: cached keys [rlo, ce) in blocks of 32, then (if this chunk holds
+    // them) the new tokens [max(rlo, P), rhi) as one more block.
+    const int ce = min(c.rhi, c.P);
+    const int n_cache_blk = ce > c.rlo ? (ce - c.rlo + kKb - 1) / kKb : 0;
+    const int new_lo = max(c.rlo, c.P);
+    const int nblk = n_cache_blk + (c.rhi > new_lo ? 1 : 0);
     const int window = a.window;
+    const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
+    const int kr_key = key_of_row(r);
 
-    for (int j = wave; j < nblk; j += kWaves) {
-        const int kb = c.rlo + j * kKb;
-        // K: A-row r holds key key_of_row(r); k-step s reads dims (2s+hh)*8 .. +7.
-        uint4 kf[kDqk / 16];
-        {
-            const uint16_t *row = key_row(a, c, kb + key_of_row(r), kc, kn, kDqk);
+    auto block_base = [&](int j) { return j < n_cache_blk ? c.rlo + j * kKb : new_lo; };
+    auto load_kv = [&](int j, KVRegs &x) {
+        const int kb = block_base(j);
+        if (j < n_cache_blk) {  // wave-uniform
+            const int p = kb + kr_key;
+            const int slot = a.ring ? p % a.cap : p;
+            const uint32_t off = p < ce ? (uint32_t)slot * kDqk * 2 + (uint32_t)hh * 16 : kOob;
 #pragma unroll
             for (int s = 0; s < kDqk / 16; ++s)
-                kf[s] = row ? *(const uint4 *)(row + (2 * s + hh) * 8) : make_uint4(0, 0, 0, 0);
-        }
-        // V: keys 16*hh + i (i < 16), dims 4r .. 4r+3.
-        uint2 vf[16];
+                x.k[s] = buf_load16(kc, off + (uint32_t)s * 32);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint16_t *row = key_row(a, c, kb + 16 * hh + i, vc, vn, kDv);
-            vf[i] = row ? *(const uint2 *)(row + 4 * r) : make_uint2(0, 0);
+            for (int i = 0; i < 16; ++i) {
+                const int pv = kb + 16 * hh + i;
+                const int sv = a.ring ? pv % a.cap : pv;
+                const uint32_t ov = pv < ce ? (uint32_t)sv * kDv * 2 + (uint32_t)r * 8 : kOob;
+                x.v[i] = buf_load8(vc, ov);
+            }
+        } else {
+            const int p = kb + kr_key;
+            const uint32_t off = p < c.rhi ? (uint32_t)(p - c.P) * krow + (uint32_t)hh * 16 : kOob;
+#pragma unroll
+            for (int s = 0; s < kDqk / 16; ++s)
+                x.k[s] = buf_load16(kn, off + (uint32_t)s * 32);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int pv = kb + 16 * hh + i;
+                const uint32_t ov = pv < c.rhi ? (uint32_t)(pv - c.P) * vrow + (uint32_t)r * 8 : kOob;
+                x.v[i] = buf_load8(vn, ov);
+            }
         }
-
+    };
+    auto compute = [&](int j, const KVRegs &x) {
+        const int kb = block_base(j);
+        const int kend = j < n_cache_blk ? ce : c.rhi;
         f32x16 sc[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
@@ -164,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, flo
         for (int s = 0; s < kDqk / 16; ++s)
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
-                sc[cb] = mfma32x32x16(as_bf16x8(kf[s]), qf[cb][s], sc[cb]);
+                sc[cb] = mfma32x32x16(as_bf16x8(x.k[s]), qf[cb][s], sc[cb]);
 
         // V^T operands: block db (dims 4*row + db), k-step t (keys 16hh + 8t + e).
         bf16x8 va[4][2];
@@ -175,60 +202,97 @@ __global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, flo
                 uint32_t w[4];
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
-                    const uint2 lo = vf[8 * t + 2 * e2], hi = vf[8 * t + 2 * e2 + 1];
+                    const uint2 lo = x.v[8 * t + 2 * e2], hi = x.v[8 * t + 2 * e2 + 1];
                     const uint32_t wl = (db < 2) ? lo.x : lo.y;
                     const uint32_t wh = (db < 2) ? hi.x : hi.y;
-                    const uint32_t a16 = (db & 1) ? (wl >> 16) : (wl & 0xffffu);
-                    const uint32_t b16 = (db & 1) ? (wh >> 16) : (wh & 0xffffu);
-                    w[e2] = a16 | (b16 << 16);
+                    w[e2] = (db & 1) ? __builtin_amdgcn_perm(wh, wl, 0x07060302u)
+                                     : __builtin_amdgcn_perm(wh, wl, 0x05040100u);
                 }
                 va[db][t] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
             }
 
+        // Cached blocks are fully visible unless they cut the range end or the
+        // window start of a later query; the new-token block is causal.
+        const bool full = j < n_cache_blk && kb + kKb <= ce &&
+                          (window <= 0 || kb >= c.P + nq - window);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            float x[16];
-            float bm = -INFINITY;
             const int qp = qpos[cb];
+            if (!full) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int p = kb + 16 * hh + i;
-                const bool vis = p < c.rhi && p <= qp && (window <= 0 || qp - p < window);
-                x[i] = vis ? sc[cb][i] * scale_log2 : -INFINITY;
-                bm = fmaxf(bm, x[i]);
+                for (int i = 0; i < 16; ++i) {
+                    const int p = kb + 16 * hh + i;
+                    const bool vis = p < kend && p <= qp && (window <= 0 || qp - p < window);
+                    sc[cb][i] = vis ? sc[cb][i] : -INFINITY;
+                }
             }
-            bm = max_across_halves(bm);
-            const float mn = fmaxf(m[cb], bm);
-            const float mu = (mn == -INFINITY) ? 0.f : mn;
-            const float alpha = fast_exp2(m[cb] - mu);
-            float ps = 0.f;
+            if (qp < 0) {  // padding column (only in the last column block)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                x[i] = fast_exp2(x[i] - mu);
-                ps += x[i];
+                for (int i = 0; i < 16; ++i)
+                    sc[cb][i] = -INFINITY;
             }
-            l[cb] = l[cb] * alpha + ps;
+            float bm = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                bm = fmaxf(bm, sc[cb][i]);
+            bm = max_across_halves(bm) * scale_log2;
+            const bool up = bm > m[cb] + kRescaleSlack || (m[cb] == -INFINITY && bm > -INFINITY);
+            const float mn = up ? bm : m[cb];
+            const float alpha = up ? fast_exp2(m[cb] - mn) : 1.f;
             m[cb] = mn;
+            const float mu = (mn == -INFINITY) ? 0.f : mn;
+            float ps = 0.f;
             bf16x8 pb[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int i = 0; i < 16; ++i) {
+                const float pr = fast_exp2(__fmaf_rn(sc[cb][i], scale_log2, -mu));
+                ps += pr;
+                pb[i >> 3][i & 7] = (__bf16)pr;
+            }
+            l[cb] = __fmaf_rn(l[cb], alpha, ps);
+            if (__builtin_amdgcn_ballot_w64(up) != 0) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pb[t][e] = (__bf16)x[8 * t + e];
+                for (int db = 0; db < 4; ++db)
+                    acc[cb][db] *= alpha;
+            }
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                acc[cb][db] *= alpha;
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
                     acc[cb][db] = mfma32x32x16(va[db][t], pb[t], acc[cb][db]);
+        }
+    };
+
+    // Blocks j = wave, wave+4, ...  With one column block, two register sets keep
+    // the loads of a wave's next block in flight while it computes the current
+    // one; with two column blocks the registers only hold one set.
+    if constexpr (NCB == 1) {
+        KVRegs x0, x1;
+        int j = wave;
+        if (j < nblk)
+            load_kv(j, x0);
+        for (; j < nblk; j += 2 * kWaves) {
+            if (j + kWaves < nblk)
+                load_kv(j + kWaves, x1);
+            compute(j, x0);
+            if (j + kWaves < nblk) {
+                if (j + 2 * kWaves < nblk)
+                    load_kv(j + 2 * kWaves, x0);
+                compute(j + kWaves, x1);
             }
+        }
+    } else {
+        for (int j = wave; j < nblk; j += kWaves) {
+            KVRegs x;
+            load_kv(j, x);
+            compute(j, x);
         }
     }
 
     // Merge the 4 waves' states, one column block at a time: waves 1..3 park
     // (acc, m, l) in LDS, wave 0 folds them into its registers and writes.
     const bool write_final = a.n_splits == 1;
-    const size_t rows_total = (size_t)a.B * a.nq * a.Hq;
+    const size_t rows_total = (size_t)a.B * nq * a.Hq;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int ncol = min(32, n_cols - cb * 32);
@@ -253,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, flo
             const int col = cb * 32 + r;
             const int t = col / group;
             const int h = c.g * group + col % group;
-            const size_t row = ((size_t)c.b * a.nq + t) * a.Hq + h;
+            const size_t row = ((size_t)c.b * nq + t) * a.Hq + h;
             float mx = m[cb];
 #pragma unroll
             for (int w = 0; w < kWaves - 1; ++w)

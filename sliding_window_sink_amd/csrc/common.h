@@ -63,6 +63,9 @@ __device__ __forceinline__ BufRsrc make_buf(const void *base, uint64_t bytes) {
 __device__ __forceinline__ uint4 buf_load16(BufRsrc r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+__device__ __forceinline__ uint2 buf_load8(BufRsrc r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 __device__ __forceinline__ void buf_store16(BufRsrc r, uint32_t off, uint4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
 }
