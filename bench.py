@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--prewarm-s", type=float, default=1.0,
                    help="untimed seconds of steps before the warm-up steps (clock ramp)")
     p.add_argument("--only", default="", help="comma list of: swa,global,decode,verify")
+    p.add_argument("--counter-pass", action="store_true",
+                   help="for rocprofv3 --pmc runs: one 1 GiB device copy (the calibration "
+                        "kernel of known traffic), then 3 launches of the headline kernel")
     return p.parse_args()
 
 
@@ -121,7 +124,7 @@ def traffic_from_profile(sha: str, launches_bytes: float):
 
 # ----------------------------------------------------------------------------- workloads
 
-def run_swa_prefill(torch, ops, synth, steps, warmup, dev, prewarm_s=1.0):
+def run_swa_prefill(torch, ops, synth, steps, warmup, dev, prewarm_s=1.0, fused_only=False):
     """Headline step: the fused kernel (RoPE of q and k applied on load, rotated k
     written out, attention); the same bits as rope(q), rope(k), prefill_swa.  The
     unfused three-kernel step is timed afterwards for reference."""
@@ -158,6 +161,8 @@ def run_swa_prefill(torch, ops, synth, steps, warmup, dev, prewarm_s=1.0):
     wall = time.perf_counter() - t0
     kern_ms = kt.mean_ms()
 
+    if fused_only:  # counter pass: only the fused kernel
+        return dict(kernel_ms=kern_ms), None
     # unfused reference step on copies (q, k rotated in place each rep: same work)
     qu, ku = q.clone(), k.clone()
     ut, rt = Timer(torch), Timer(torch)
@@ -442,6 +447,18 @@ def main():
     torch.cuda.set_device(dev)
     only = set(args.only.split(",")) if args.only else {"swa", "global", "decode", "verify"}
 
+    if args.counter_pass:
+        # calibration: a plain copy moves exactly 1 GiB in and 1 GiB out
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        run_swa_prefill(torch, ops, synth, steps=3, warmup=0, dev=dev, prewarm_s=0.0,
+                        fused_only=True)
+        torch.cuda.synchronize()
+        log("[bench] counter pass done")
+        return
     log("[bench] SWA prefill T=32768: warmup %d, steps %d" % (args.warmup, args.steps))
     res, inputs = run_swa_prefill(torch, ops, synth, args.steps, args.warmup, dev, args.prewarm_s)
     ms = res["ms_per_step"]
