@@ -38,7 +38,7 @@ METRIC = "prefill TFLOP/s (in-window) & %MFMA peak; decode KV GB/s & %HBM peak"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-others", action="store_true", help="skip the other workloads")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -138,11 +138,8 @@ def run_swa_prefill(torch, ops, synth, steps, warmup, dev, prewarm_s=1.0, fused_
     o = torch.empty(B, T, Hq, 128, dtype=torch.bfloat16, device=dev)
     k_rot = torch.empty_like(k)
 
-    kt = Timer(torch)
-
     def step():
-        with kt:
-            ops.prefill_swa_rope(q, k, v, sink, w.window, w.base, k_rot=k_rot, out=o)
+        ops.prefill_swa_rope(q, k, v, sink, w.window, w.base, k_rot=k_rot, out=o)
 
     # bring the GPU clocks up before the W warm-up steps (untimed): a few ms of
     # work after the data generation is not enough to leave the idle clock
@@ -152,14 +149,20 @@ def run_swa_prefill(torch, ops, synth, steps, warmup, dev, prewarm_s=1.0, fused_
         torch.cuda.synchronize()
     for _ in range(warmup):
         step()
-    kt.pairs.clear()
+    # Timed region: K back-to-back launches of the one kernel on torch's current
+    # stream (the stream the library launches on), bracketed by synchronize on the
+    # host and by one HIP event pair on the stream: mean launch = elapsed / K.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for _ in range(steps):
         step()
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = kt.mean_ms()
+    kern_ms = ev0.elapsed_time(ev1) / steps
 
     if fused_only:  # counter pass: only the fused kernel
         return dict(kernel_ms=kern_ms), None

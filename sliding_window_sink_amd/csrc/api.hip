@@ -156,11 +156,11 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
             int64_t c = (span + num_splits - 1) / num_splits;
             chunk = (int)((c + 127) / 128 * 128);
         } else {
-            // automatic: ~16 workgroups per compute unit over the longest sequence,
+            // automatic: ~32 workgroups per compute unit over the longest sequence,
             // but chunks long enough that the partial states stay a few percent of
             // the K/V bytes they summarise (520 B per column vs 640 B per key).
             const int64_t cus = device_cu_count();
-            int64_t c = ((int64_t)B * Hkv * span + 16 * cus - 1) / (16 * cus);
+            int64_t c = ((int64_t)B * Hkv * span + 32 * cus - 1) / (32 * cus);
             c = std::max<int64_t>(c, 28 * (int64_t)n_cols);
             c = (c + 127) / 128 * 128;
             const int64_t want = (span + c - 1) / c;

@@ -469,7 +469,11 @@ hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s) {
     const int n_cols = a.nq * (a.Hq / a.Hkv);
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 grid((unsigned)(a.B * a.Hkv * a.n_splits)), block(kThreads);
-    if (n_cols <= 32)
+    if (n_cols <= 16) {
+        const hipError_t e16 = launch_decode16(a, s);
+        if (e16 != hipSuccess)
+            return e16;
+    } else if (n_cols <= 32)
         cached_bf16_kernel<1><<<grid, block, 0, s>>>(a, scale_log2);
     else
         cached_bf16_kernel<2><<<grid, block, 0, s>>>(a, scale_log2);

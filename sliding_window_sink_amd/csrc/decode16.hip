@@ -1,0 +1,355 @@
+// decode16.hip -- decode sink attention with 16-column MFMA tiles (gfx950, bf16).
+//
+// Same operation as cached.hip (MiMo-V2-Flash Technical Report, Section 2.2
+// sink softmax; Section 2.3.1 one new token per step over a per-request
+// cache), for the case where the (token, head) columns of one KV group number
+// at most 16: a decode step of a global layer (16 query heads per KV head,
+// Table 1) or of an SWA layer (8), or a 2-token verify of an SWA layer.
+//
+// Why a second kernel: decode is HBM bound (16 FLOP per byte), and with only
+// 16 columns the 32x32 MFMA tile of cached.hip wastes half its columns and,
+// more importantly, its 64-column accumulators force one wave per SIMD.  With
+// v_mfma_f32_16x16x32_bf16 the per-wave state halves (Q^T 24 registers, O^T 32)
+// so two waves per SIMD fit, and the operand layouts give better HBM access:
+//   - A = K (16 keys x 32 dims per MFMA): lane l owns key l%16 and reads 16
+//     bytes at dims 32s + 8(l/16): four lanes cover 64 contiguous bytes;
+//   - A = V^T (16 output dims x 32 keys): the output-dim order is chosen as
+//     dim = 8*row + tile, so lane (row, group) loads 16 contiguous bytes (8
+//     dims) of each of its 8 keys -- every load instruction reads 4 whole
+//     256-byte V rows -- and an 8x8 register transpose builds the 8 operands;
+//   - C = S^T (16 keys x 16 columns): lane l owns column l%16, keys 4(l/16)+i;
+//     the P^T operand is taken straight from those registers.
+// Everything else follows cached.hip: a workgroup of 4 waves per (sequence, KV
+// group, context chunk), blocks of 32 keys taken by the waves in turn, online
+// softmax without the sink per wave, an LDS merge that adds the sink (one
+// chunk) or writes unnormalised partials for the split-K combine; decode stores
+// the new token into the cache in the same launch (the attention reads
+// positions >= P from k_new).  Chunks that hold no key return at once: the
+// combine only reads the chunks that intersect the visible range.
+#include "common.h"
+
+namespace sinkattn {
+namespace {
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kKb = 32;
+constexpr int kCols = 16;
+constexpr int kMergeStride = kDv + 4;
+constexpr uint32_t kOob = 0x80000000u;  // an offset past every descriptor: reads 0
+
+__device__ __forceinline__ f32x4v mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4v &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct KV16 {
+    uint4 k[2][kDqk / 32];  // key tile kt (keys 16kt + l%16), k-step s: dims 32s + 8(l/16) .. +7
+    uint4 v[8];             // key (e/4)*16 + 4(l/16) + e%4, dims 8(l%16) .. +7
+};
+
+__global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, float scale_log2) {
+    __shared__ __attribute__((aligned(16))) float merge[kWaves - 1][kCols][kMergeStride];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, kg = lane >> 4;
+    const int split = blockIdx.x % a.n_splits;
+    const int bg = blockIdx.x / a.n_splits;
+    const int Hkv = a.Hkv, nq = a.nq, Hq = a.Hq;
+    const int g = bg % Hkv, b = bg / Hkv;
+    const int group = Hq / Hkv;
+    const int n_cols = nq * group;
+    const int P = clamp_len(a.cache_len[b], a.max_len);
+    const int lo = a.window > 0 ? max(0, P - a.window + 1) : 0;
+    const int hi = P + nq;
+    int rlo = lo, rhi = hi;
+    if (a.n_splits > 1) {
+        rlo = max(lo, split * a.chunk);
+        rhi = min(hi, (split + 1) * a.chunk);
+    }
+
+    const size_t crow0 = ((size_t)b * Hkv + g) * a.cap;
+    const size_t nrow0 = (size_t)b * nq * Hkv + g;  // row of new token t: nrow0 + t*Hkv
+
+    // Decode: the chunk holding position P stores the new token (slot / index P).
+    if (a.write_new && P >= rlo && P < rhi && (a.ring || P < a.cap)) {
+        const int slot = a.ring ? (P % a.cap) : P;
+        uint16_t *kd = (uint16_t *)a.k_cache + (crow0 + slot) * kDqk;
+        uint16_t *vd = (uint16_t *)a.v_cache + (crow0 + slot) * kDv;
+        const uint16_t *ks = (const uint16_t *)a.k_new + nrow0 * kDqk;
+        const uint16_t *vs = (const uint16_t *)a.v_new + nrow0 * kDv;
+        if (tid < kDqk / 8)
+            *(uint4 *)(kd + tid * 8) = *(const uint4 *)(ks + tid * 8);
+        else if (tid < kDqk / 8 + kDv / 8)
+            *(uint4 *)(vd + (tid - kDqk / 8) * 8) = *(const uint4 *)(vs + (tid - kDqk / 8) * 8);
+    }
+    if (rlo >= rhi)
+        return;  // uniform: this chunk holds no visible key
+
+    const uint64_t cache_rows = a.ring ? (uint64_t)a.cap : (uint64_t)P;
+    const BufRsrc kc = make_buf((const uint16_t *)a.k_cache + crow0 * kDqk, cache_rows * kDqk * 2);
+    const BufRsrc vc = make_buf((const uint16_t *)a.v_cache + crow0 * kDv, cache_rows * kDv * 2);
+    const BufRsrc kn = make_buf((const uint16_t *)a.k_new + nrow0 * kDqk,
+                                ((uint64_t)(nq - 1) * Hkv + 1) * kDqk * 2);
+    const BufRsrc vn = make_buf((const uint16_t *)a.v_new + nrow0 * kDv,
+                                ((uint64_t)(nq - 1) * Hkv + 1) * kDv * 2);
+
+    // Q^T operand (B of the QK MFMA): column lr = (token t, head) = divmod(lr, group).
+    const bool col_ok = lr < n_cols;
+    const int qpos = col_ok ? P + lr / group : -1;
+    bf16x8 qf[kDqk / 32];
+    {
+        const BufRsrc qb = make_buf((const uint16_t *)a.q + (size_t)b * nq * Hq * kDqk,
+                                    (uint64_t)nq * Hq * kDqk * 2);
+        const uint32_t off =
+            col_ok ? ((uint32_t)((lr / group) * Hq + g * group + lr % group) * kDqk + (uint32_t)kg * 8) * 2
+                   : kOob;
+#pragma unroll
+        for (int s = 0; s < kDqk / 32; ++s)
+            qf[s] = as_bf16x8(buf_load16(qb, off + (uint32_t)s * 64));
+    }
+
+    float m = -INFINITY, l = 0.f;
+    f32x4v acc[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+        acc[db] = f32x4v{};
+
+    const int ce = min(rhi, P);
+    const int n_cache_blk = ce > rlo ? (ce - rlo + kKb - 1) / kKb : 0;
+    const int new_lo = max(rlo, P);
+    const int nblk = n_cache_blk + (rhi > new_lo ? 1 : 0);
+    const int window = a.window;
+    const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
+
+    auto block_base = [&](int j) { return j < n_cache_blk ? rlo + j * kKb : new_lo; };
+    // K and V of block j are loaded separately: the K registers are reloaded
+    // for the wave's next block as soon as QK has consumed them, the V registers
+    // after PV, so one register set keeps loads in flight through the compute.
+    // Cache blocks and the new-token block use separate functions so that every
+    // load names one descriptor.
+    auto load_k = [&](int j, KV16 &x) {
+        const int kb = rlo + j * kKb;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int p = kb + 16 * kt + lr;
+            const int slot = a.ring ? p % a.cap : p;
+            const uint32_t off = p < ce ? (uint32_t)slot * kDqk * 2 + (uint32_t)kg * 16 : kOob;
+#pragma unroll
+            for (int s = 0; s < kDqk / 32; ++s)
+                x.k[kt][s] = buf_load16(kc, off + (uint32_t)s * 64);
+        }
+    };
+    auto load_v = [&](int j, KV16 &x) {
+        const int kb = rlo + j * kKb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int p = kb + (e >> 2) * 16 + 4 * kg + (e & 3);
+            const int slot = a.ring ? p % a.cap : p;
+            const uint32_t off = p < ce ? (uint32_t)slot * kDv * 2 + (uint32_t)lr * 16 : kOob;
+            x.v[e] = buf_load16(vc, off);
+        }
+    };
+    auto load_new = [&](KV16 &x) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int p = new_lo + 16 * kt + lr;
+            const uint32_t off = p < rhi ? (uint32_t)(p - P) * krow + (uint32_t)kg * 16 : kOob;
+#pragma unroll
+            for (int s = 0; s < kDqk / 32; ++s)
+                x.k[kt][s] = buf_load16(kn, off + (uint32_t)s * 64);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int p = new_lo + (e >> 2) * 16 + 4 * kg + (e & 3);
+            const uint32_t off = p < rhi ? (uint32_t)(p - P) * vrow + (uint32_t)lr * 16 : kOob;
+            x.v[e] = buf_load16(vn, off);
+        }
+    };
+    auto compute = [&](int j, int jn, KV16 &x) {
+        const int kb = block_base(j);
+        const int kend = j < n_cache_blk ? ce : rhi;
+        f32x4v sc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            sc[kt] = f32x4v{};
+#pragma unroll
+            for (int s = 0; s < kDqk / 32; ++s)
+                sc[kt] = mfma16x16x32(as_bf16x8(x.k[kt][s]), qf[s], sc[kt]);
+        }
+        if (jn < n_cache_blk)
+            load_k(jn, x);
+        // element e of this lane: key kb + (e/4)*16 + 4*kg + e%4, column lr
+        const bool full = j < n_cache_blk && kb + kKb <= ce && (window <= 0 || kb >= P + nq - window);
+        float xs[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = sc[e >> 2][e & 3];
+            if (!full) {
+                const int p = kb + (e >> 2) * 16 + 4 * kg + (e & 3);
+                const bool vis = p < kend && p <= qpos && (window <= 0 || qpos - p < window);
+                v = vis ? v : -INFINITY;
+            }
+            xs[e] = col_ok ? v : -INFINITY;
+        }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            bm = fmaxf(bm, xs[e]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        bm *= scale_log2;
+        const bool up = bm > m + kRescaleSlack || (m == -INFINITY && bm > -INFINITY);
+        const float mn = up ? bm : m;
+        const float alpha = up ? fast_exp2(m - mn) : 1.f;
+        m = mn;
+        const float mu = (mn == -INFINITY) ? 0.f : mn;
+        float ps = 0.f;
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float pr = fast_exp2(__fmaf_rn(xs[e], scale_log2, -mu));
+            ps += pr;
+            pb[e] = (__bf16)pr;
+        }
+        l = __fmaf_rn(l, alpha, ps);
+        if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+                acc[db] *= alpha;
+        }
+        // V^T operand of tile db: element e = V[key(e)][8*lr + db]; x.v[e] holds dims
+        // 8lr..8lr+7 of key(e), so each operand word pairs one 16-bit half of two loads.
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const uint4 va0 = x.v[2 * e2], va1 = x.v[2 * e2 + 1];
+                const uint32_t wa = (db >> 1) == 0 ? va0.x : (db >> 1) == 1 ? va0.y : (db >> 1) == 2 ? va0.z : va0.w;
+                const uint32_t wb = (db >> 1) == 0 ? va1.x : (db >> 1) == 1 ? va1.y : (db >> 1) == 2 ? va1.z : va1.w;
+                w[e2] = (db & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u)
+                                 : __builtin_amdgcn_perm(wb, wa, 0x05040100u);
+            }
+            acc[db] = mfma16x16x32(as_bf16x8(make_uint4(w[0], w[1], w[2], w[3])), pb, acc[db]);
+        }
+        if (jn < n_cache_blk)
+            load_v(jn, x);
+    };
+
+    // Cache blocks j = wave, wave+4, ..., then the new-token block (index
+    // n_cache_blk) on the wave it falls to.  At about 200 registers two waves
+    // share each SIMD (a second register set per wave measured slower: one wave
+    // per SIMD).
+    {
+        KV16 x;
+        if (wave < n_cache_blk) {
+            load_k(wave, x);
+            load_v(wave, x);
+        }
+        for (int j = wave; j < n_cache_blk; j += kWaves)
+            compute(j, j + kWaves, x);
+        if (nblk > n_cache_blk && n_cache_blk % kWaves == wave) {
+            load_new(x);
+            compute(n_cache_blk, nblk, x);
+        }
+    }
+
+    // l is per lane group (16 lanes) -> total over the 4 groups of the column
+    float lt = l + __shfl_xor(l, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+
+    // merge: waves 1..3 park (acc, m, l) in LDS; wave 0 folds them in and writes.
+    // acc[db][i] holds dim 8*(4kg + i) + db of column lr.
+    if (wave > 0 && col_ok) {
+        float *e = &merge[wave - 1][lr][0];
+        if (kg == 0) {
+            e[kDv] = m;
+            e[kDv + 1] = lt;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 8 * (4 * kg + i);
+            *(float4 *)&e[d0] = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+            *(float4 *)&e[d0 + 4] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && col_ok) {
+        const bool write_final = a.n_splits == 1;
+        const size_t rows_total = (size_t)a.B * nq * Hq;
+        const int t = lr / group;
+        const int h = g * group + lr % group;
+        const size_t row = ((size_t)b * nq + t) * Hq + h;
+        float mx = m;
+#pragma unroll
+        for (int w = 0; w < kWaves - 1; ++w)
+            mx = fmaxf(mx, merge[w][lr][kDv]);
+        float M = mx, zs = 0.f;
+        if (write_final) {
+            const float sink2 = a.sink[h] * kLog2e;
+            M = fmaxf(mx, sink2);
+            zs = (sink2 == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(sink2 - M);
+        }
+        const float f0 = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+        float fw[kWaves - 1];
+        float z = zs + lt * f0;
+#pragma unroll
+        for (int w = 0; w < kWaves - 1; ++w) {
+            const float mw = merge[w][lr][kDv];
+            fw[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+            z += merge[w][lr][kDv + 1] * fw[w];
+        }
+        const float so = write_final ? (z > 0.f ? 1.f / z : 0.f) : 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 8 * (4 * kg + i);
+            float vals[8];
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+                vals[db] = acc[db][i] * f0;
+#pragma unroll
+            for (int w = 0; w < kWaves - 1; ++w) {
+                const float4 p0 = *(const float4 *)&merge[w][lr][d0];
+                const float4 p1 = *(const float4 *)&merge[w][lr][d0 + 4];
+                vals[0] += p0.x * fw[w];
+                vals[1] += p0.y * fw[w];
+                vals[2] += p0.z * fw[w];
+                vals[3] += p0.w * fw[w];
+                vals[4] += p1.x * fw[w];
+                vals[5] += p1.y * fw[w];
+                vals[6] += p1.z * fw[w];
+                vals[7] += p1.w * fw[w];
+            }
+            if (write_final) {
+                uint4 u;
+                u.x = pack_bf16x2(vals[0] * so, vals[1] * so);
+                u.y = pack_bf16x2(vals[2] * so, vals[3] * so);
+                u.z = pack_bf16x2(vals[4] * so, vals[5] * so);
+                u.w = pack_bf16x2(vals[6] * so, vals[7] * so);
+                *(uint4 *)((uint16_t *)a.o + row * kDv + d0) = u;
+            } else {
+                float *dst = &a.ws[2 * rows_total * a.n_splits + (row * a.n_splits + split) * kDv + d0];
+                *(float4 *)dst = make_float4(vals[0], vals[1], vals[2], vals[3]);
+                *(float4 *)(dst + 4) = make_float4(vals[4], vals[5], vals[6], vals[7]);
+            }
+        }
+        if (!write_final && kg == 0) {
+            const size_t slot = row * a.n_splits + split;
+            a.ws[slot] = M;
+            a.ws[rows_total * a.n_splits + slot] = (M == -INFINITY) ? 0.f : z;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode16(const CachedArgs &a, hipStream_t s) {
+    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    const dim3 grid((unsigned)(a.B * a.Hkv * a.n_splits)), block(kThreads);
+    decode16_kernel<<<grid, block, 0, s>>>(a, scale_log2);
+    return hipGetLastError();
+}
+
+}  // namespace sinkattn

@@ -56,6 +56,9 @@ constexpr int kSwaMaxWindow = 129;
 hipError_t launch_prefill_swa_persistent(const PrefillArgs &a, double rope_base, void *k_rot,
                                          bool rope, hipStream_t s);
 hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s);
+// Attention part of launch_cached_bf16 for at most 16 columns per KV group
+// (no split-K combine).
+hipError_t launch_decode16(const CachedArgs &a, hipStream_t s);
 hipError_t launch_cached_f32(const CachedArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int bf16, hipStream_t s);
 
