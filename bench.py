@@ -203,20 +203,29 @@ def run_global_prefill(torch, ops, synth, dev, reps=5):
     sink = synth.device_normal(w.seed + 3, (Hq,), torch.float32, device=dev)
     pos = synth.positions(B, T).to(dev)
     o = torch.empty(B, T, Hq, 128, dtype=torch.bfloat16, device=dev)
-    kt, rt = Timer(torch), Timer(torch)
-    ops.prefill_global(q, k, v, sink, out=o)  # warm-up
+    k_rot = torch.empty_like(k)
+    # the step: partial RoPE fused (k rotated once into k_rot, q on load)
+    ft, kt, rt = Timer(torch), Timer(torch), Timer(torch)
+    ops.prefill_global_rope(q, k, v, sink, w.base, k_rot=k_rot, out=o)  # warm-up
+    for _ in range(reps):
+        with ft:
+            ops.prefill_global_rope(q, k, v, sink, w.base, k_rot=k_rot, out=o)
+    # the same work unfused: two RoPE passes, then the plain attention kernel
+    qr, kr = q.clone(), k.clone()
     for _ in range(reps):
         with rt:
-            ops.rope_partial(q, pos, w.base)
-            ops.rope_partial(k, pos, w.base)
+            ops.rope_partial(qr, pos, w.base)
+            ops.rope_partial(kr, pos, w.base)
         with kt:
-            ops.prefill_global(q, k, v, sink, out=o)
-    kms, rms = kt.mean_ms(), rt.mean_ms()
+            ops.prefill_global(qr, kr, v, sink, out=o)
+    fms, kms, rms = ft.mean_ms(), kt.mean_ms(), rt.mean_ms()
     flops = global_pairs(T) * B * Hq * FLOP_PER_PAIR_HEAD
-    del q, k, v, o
-    return dict(workload=w.name, kernel_ms=kms, rope_ms=rms, step_ms=kms + rms,
-                tflops_kernel=flops / kms / 1e9, tflops_step=flops / (kms + rms) / 1e9,
-                mfma_frac_kernel=flops / kms / 1e9 / PEAK_BF16_TFLOPS, flops=flops)
+    del q, k, v, o, qr, kr, k_rot
+    return dict(workload=w.name, step="prefill_global_rope (RoPE fused)", step_ms=fms,
+                tflops_step=flops / fms / 1e9, mfma_frac_step=flops / fms / 1e9 / PEAK_BF16_TFLOPS,
+                kernel_ms=kms, tflops_kernel=flops / kms / 1e9,
+                mfma_frac_kernel=flops / kms / 1e9 / PEAK_BF16_TFLOPS,
+                unfused_rope_ms=rms, unfused_step_ms=kms + rms, flops=flops)
 
 
 def _graph_time(torch, fn, reps=20):
@@ -274,13 +283,15 @@ def run_hybrid_decode(torch, ops, synth, dev):
     ws = torch.empty(ops.decode_workspace_bytes(B, Hq, 1, 256) // 4, dtype=torch.float32,
                      device=dev)
 
+    # each layer: RoPE of the new token fused, attention, new token stored in the cache
     def swa(r):
-        ops.decode(r["q"], r["kn"], r["vn"], r["kc"], r["vc"], cl_d, r["sink"], ops.RING, 128,
-                   max_len, out=r["o"])
+        ops.decode_rope(r["q"], r["kn"], r["vn"], r["kc"], r["vc"], cl_d, r["sink"], ops.RING,
+                        128, max_len, base=synth.BASE_SWA, out=r["o"])
 
     def glob():
-        ops.decode(gl["q"], gl["kn"], gl["vn"], gl["kc"], gl["vc"], cl_d, gl["sink"], ops.CONTIG,
-                   0, max_len, num_splits=0, workspace=ws, out=gl["o"])
+        ops.decode_rope(gl["q"], gl["kn"], gl["vn"], gl["kc"], gl["vc"], cl_d, gl["sink"],
+                        ops.CONTIG, 0, max_len, base=synth.BASE_GA, num_splits=0, workspace=ws,
+                        out=gl["o"])
 
     def block():
         for r in rings:
@@ -323,7 +334,6 @@ def run_verify(torch, ops, synth, dev):
     cl = torch.full((B,), L, dtype=torch.int32)
     cl_d = cl.to(dev)
     s0 = w.seed * 100
-    pos = synth.positions(B, nq, L).to(dev)
     swa = dict(q=synth.device_normal(s0, (B, nq, Hq, 192), device=dev),
                kn=synth.device_normal(s0 + 1, (B, nq, 8, 192), device=dev),
                vn=synth.device_normal(s0 + 2, (B, nq, 8, 128), device=dev),
@@ -345,29 +355,28 @@ def run_verify(torch, ops, synth, dev):
     # decode baseline for the verify/decode ratio: same caches, one query token
     kc1 = gl["kc"]
 
-    def rope_new():
-        for d in (swa, gl):
-            ops.rope_partial(d["q"], pos, synth.BASE_SWA if d is swa else synth.BASE_GA)
-            ops.rope_partial(d["kn"], pos, synth.BASE_SWA if d is swa else synth.BASE_GA)
+    # RoPE of the draft tokens fused; the rotated keys go to k_rot for kv_append
+    kr_s, kr_g = torch.empty_like(swa["kn"]), torch.empty_like(gl["kn"])
 
     def v_swa():
-        ops.verify(swa["q"], swa["kn"], swa["vn"], swa["kc"], swa["vc"], cl_d, swa["sink"],
-                   ops.RING, 128, L, out=swa["o"])
+        ops.verify_rope(swa["q"], swa["kn"], swa["vn"], swa["kc"], swa["vc"], cl_d, swa["sink"],
+                        ops.RING, 128, L, base=synth.BASE_SWA, k_rot=kr_s, out=swa["o"])
 
     def v_glob():
-        ops.verify(gl["q"], gl["kn"], gl["vn"], gl["kc"], gl["vc"], cl_d, gl["sink"], ops.CONTIG,
-                   0, L, num_splits=0, workspace=ws, out=gl["o"])
+        ops.verify_rope(gl["q"], gl["kn"], gl["vn"], gl["kc"], gl["vc"], cl_d, gl["sink"],
+                        ops.CONTIG, 0, L, base=synth.BASE_GA, k_rot=kr_g, num_splits=0,
+                        workspace=ws, out=gl["o"])
 
     q1, kn1, vn1 = (gl["q"][:, 0:1].contiguous(), gl["kn"][:, 0:1].contiguous(),
                     gl["vn"][:, 0:1].contiguous())
     o1 = torch.empty(B, 1, Hq, 128, dtype=torch.bfloat16, device=dev)
+    kr1 = torch.empty_like(kn1)
 
     def d_glob():
-        ops.verify(q1, kn1, vn1, kc1, gl["vc"], cl_d, gl["sink"], ops.CONTIG, 0, L,
-                   num_splits=0, workspace=ws, out=o1)
+        ops.verify_rope(q1, kn1, vn1, kc1, gl["vc"], cl_d, gl["sink"], ops.CONTIG, 0, L,
+                        base=synth.BASE_GA, k_rot=kr1, num_splits=0, workspace=ws, out=o1)
 
     def step():
-        rope_new()
         v_swa()
         v_glob()
 

@@ -123,6 +123,22 @@ int sinkattn_prefill_global(const void *q, const void *k, const void *v, const f
                             int dv, float scale, int dtype, void *stream);
 
 /*
+ * Global prefill with the partial RoPE fused (Section 2.1: 64 rotated dims;
+ * Section 3.2: global layers use base 6.4e5, later 5e6).  The result equals
+ * sinkattn_rope_partial(q, positions 0..T-1), the same for k, then
+ * sinkattn_prefill_global -- bit for bit.  q and k are read-only (un-rotated).
+ * k_rot [B,T,Hkv,192] is REQUIRED: the rotated keys are written there first
+ * (each key is read by every later query tile, so it is rotated once) and the
+ * attention reads them back; q is rotated on load and never written.  k_rot
+ * must not overlap any input or output.  Supported: bf16, rope_dim == 64
+ * (interleaved pairs); SINKATTN_ERR_UNSUPPORTED otherwise.
+ */
+int sinkattn_prefill_global_rope(const void *q, const void *k, const void *v, const float *sink,
+                                 void *o, float *lse, void *k_rot, int B, int T, int Hq,
+                                 int Hkv, int dqk, int dv, float scale, int rope_dim,
+                                 double rope_base, int dtype, void *stream);
+
+/*
  * Bytes of fp32 workspace that sinkattn_decode / sinkattn_verify need for a
  * split-K pass over a contiguous cache with at most `max_splits` splits:
  * B * n_q * Hq * max_splits * (dv + 2) * 4.  Zero if max_splits <= 1.
@@ -174,6 +190,34 @@ int sinkattn_verify(const void *q, const void *k_new, const void *v_new,
                     int B, int nq, int Hq, int Hkv, int dqk, int dv, int window, float scale,
                     int num_splits, void *workspace, size_t ws_bytes, int dtype,
                     void *stream);
+
+/*
+ * Decode and verify with the partial RoPE fused (Section 2.1): q and k_new are
+ * given un-rotated and read-only; token t is rotated at position P + t
+ * (P = cache_len[b]) inside the attention kernel, 64 dims, interleaved pairs,
+ * base rope_base.  Results equal sinkattn_rope_partial on q and k_new at those
+ * positions followed by sinkattn_decode / sinkattn_verify -- bit for bit:
+ *   sinkattn_decode_rope stores the ROTATED k_new (and v_new) into the cache;
+ *   sinkattn_verify_rope leaves the caches untouched and, if k_rot is non-NULL,
+ *   writes the rotated k_new there ([B,nq,Hkv,192], the input of a later
+ *   sinkattn_kv_append; it must not overlap any other argument).
+ * Other arguments as in sinkattn_decode / sinkattn_verify.  Supported: bf16,
+ * rope_dim == 64 (SINKATTN_ERR_UNSUPPORTED otherwise).
+ */
+int sinkattn_decode_rope(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                         void *v_cache, int kind, int cap, const int32_t *cache_len,
+                         int max_len_hint, const float *sink, void *o, int B, int Hq, int Hkv,
+                         int dqk, int dv, int window, float scale, int rope_dim,
+                         double rope_base, int num_splits, void *workspace, size_t ws_bytes,
+                         int dtype, void *stream);
+
+int sinkattn_verify_rope(const void *q, const void *k_new, const void *v_new,
+                         const void *k_cache, const void *v_cache, int kind, int cap,
+                         const int32_t *cache_len, int max_len_hint, const float *sink, void *o,
+                         void *k_rot, int B, int nq, int Hq, int Hkv, int dqk, int dv,
+                         int window, float scale, int rope_dim, double rope_base,
+                         int num_splits, void *workspace, size_t ws_bytes, int dtype,
+                         void *stream);
 
 /*
  * Commit accepted tokens into a cache (the step after verification).

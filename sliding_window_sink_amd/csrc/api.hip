@@ -107,10 +107,18 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
                   void *v_cache, int kind, int cap, const int32_t *cache_len, int max_len_hint,
                   const float *sink, void *o, int B, int nq, int Hq, int Hkv, int dqk, int dv,
                   int window, float scale, int num_splits, void *workspace, size_t ws_bytes,
-                  int dtype, void *stream, int write_new) {
+                  int dtype, void *stream, int write_new, int rope = 0, int rope_dim = 0,
+                  double rope_base = 0.0, void *k_rot = nullptr) {
     int st = check_heads(Hq, Hkv, dqk, dv, dtype);
     if (st)
         return st;
+    if (rope) {
+        if (!(rope_base > 0.0) || !std::isfinite(rope_base) || rope_dim < 0 ||
+            rope_dim % 2 != 0 || rope_dim > dqk)
+            return SINKATTN_ERR_SHAPE;
+        if (dtype != SINKATTN_BF16 || rope_dim != 64)
+            return SINKATTN_ERR_UNSUPPORTED;
+    }
     if (kind != SINKATTN_CACHE_RING && kind != SINKATTN_CACHE_CONTIG)
         return SINKATTN_ERR_UNSUPPORTED;
     if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_len || !sink || !o)
@@ -137,6 +145,10 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
     const size_t kcn = (size_t)B * Hkv * cap * kDqk * es, vcn = (size_t)B * Hkv * cap * kDv * es;
     const size_t qn = (size_t)B * nq * Hq * kDqk * es;
     const size_t knn = (size_t)B * nq * Hkv * kDqk * es, vnn = (size_t)B * nq * Hkv * kDv * es;
+    if (k_rot && (overlaps(k_rot, knn, q, qn) || overlaps(k_rot, knn, k_new, knn) ||
+                  overlaps(k_rot, knn, v_new, vnn) || overlaps(k_rot, knn, k_cache, kcn) ||
+                  overlaps(k_rot, knn, v_cache, vcn) || overlaps(k_rot, knn, o, on)))
+        return SINKATTN_ERR_ALIAS;
     if (overlaps(o, on, q, qn) || overlaps(o, on, k_cache, kcn) || overlaps(o, on, v_cache, vcn) ||
         overlaps(o, on, k_new, knn) || overlaps(o, on, v_new, vnn) ||
         overlaps(k_cache, kcn, v_cache, vcn) ||
@@ -178,7 +190,8 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
                 chunk = INT_MAX;
             }
         }
-        if (splits > 1 && overlaps(workspace, per_split * splits, o, on))
+        if (splits > 1 && (overlaps(workspace, per_split * splits, o, on) ||
+                           overlaps(workspace, per_split * splits, k_rot, k_rot ? knn : 0)))
             return SINKATTN_ERR_ALIAS;
     }
     if (B == 0)
@@ -206,6 +219,9 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
     a.n_splits = splits;
     a.chunk = chunk;
     a.scale = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)dqk));
+    a.rope = rope;
+    a.rope_base = rope_base;
+    a.k_rot = k_rot;
     hipStream_t s = (hipStream_t)stream;
     return status_from_hip(dtype == SINKATTN_BF16 ? launch_cached_bf16(a, s)
                                                   : launch_cached_f32(a, s));
@@ -305,6 +321,49 @@ int sinkattn_prefill_global(const void *q, const void *k, const void *v, const f
                           stream);
 }
 
+int sinkattn_prefill_global_rope(const void *q, const void *k, const void *v, const float *sink,
+                                 void *o, float *lse, void *k_rot, int B, int T, int Hq,
+                                 int Hkv, int dqk, int dv, float scale, int rope_dim,
+                                 double rope_base, int dtype, void *stream) {
+    int st = check_heads(Hq, Hkv, dqk, dv, dtype);
+    if (st)
+        return st;
+    if (!q || !k || !v || !sink || !o || !k_rot)
+        return SINKATTN_ERR_NULL_PTR;
+    if (B < 0 || T < 0 || !(rope_base > 0.0) || !std::isfinite(rope_base) || rope_dim < 0 ||
+        rope_dim % 2 != 0 || rope_dim > dqk)
+        return SINKATTN_ERR_SHAPE;
+    if (dtype != SINKATTN_BF16 || rope_dim != 64)
+        return SINKATTN_ERR_UNSUPPORTED;
+    if ((int64_t)B * T * Hq > INT_MAX || (int64_t)B * T > INT_MAX / kDqk)
+        return SINKATTN_ERR_SHAPE;
+    const size_t es = esize(dtype);
+    const size_t qn = (size_t)B * T * Hq * kDqk * es, kn = (size_t)B * T * Hkv * kDqk * es;
+    const size_t vn = (size_t)B * T * Hkv * kDv * es, on = (size_t)B * T * Hq * kDv * es;
+    const size_t ln = lse ? (size_t)B * Hq * T * 4 : 0;
+    const void *ins[3] = {q, k, v};
+    const size_t insz[3] = {qn, kn, vn};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(o, on, ins[i], insz[i]) || overlaps(lse, ln, ins[i], insz[i]) ||
+            overlaps(k_rot, kn, ins[i], insz[i]))
+            return SINKATTN_ERR_ALIAS;
+    if (overlaps(lse, ln, o, on) || overlaps(k_rot, kn, o, on) || overlaps(k_rot, kn, lse, ln))
+        return SINKATTN_ERR_ALIAS;
+    if ((size_t)B * T == 0)
+        return SINKATTN_OK;
+    hipStream_t s = (hipStream_t)stream;
+    // The keys are rotated once (T x Hkv rows, written to k_rot, read back by
+    // every query tile); q is rotated on load inside the attention kernel.
+    hipError_t e = launch_rope_rows(k, k_rot, B, T, Hkv, rope_base, s);
+    if (e != hipSuccess)
+        return SINKATTN_ERR_HIP;
+    PrefillArgs a{q, k_rot, v, sink, o, lse, B, T, Hq, Hkv, 0,
+                  scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)dqk))};
+    a.rope_q = 1;
+    a.rope_base = rope_base;
+    return status_from_hip(launch_prefill_bf16(a, s));
+}
+
 size_t sinkattn_decode_workspace_bytes(int B, int Hq, int dv, int n_q, int max_splits) {
     return ws_bytes_for(B, Hq, dv, n_q, max_splits);
 }
@@ -327,6 +386,30 @@ int sinkattn_verify(const void *q, const void *k_new, const void *v_new, const v
     return cached_common(q, k_new, v_new, (void *)k_cache, (void *)v_cache, kind, cap,
                          cache_len, max_len_hint, sink, o, B, nq, Hq, Hkv, dqk, dv, window,
                          scale, num_splits, workspace, ws_bytes, dtype, stream, 0);
+}
+
+int sinkattn_decode_rope(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                         void *v_cache, int kind, int cap, const int32_t *cache_len,
+                         int max_len_hint, const float *sink, void *o, int B, int Hq, int Hkv,
+                         int dqk, int dv, int window, float scale, int rope_dim,
+                         double rope_base, int num_splits, void *workspace, size_t ws_bytes,
+                         int dtype, void *stream) {
+    return cached_common(q, k_new, v_new, k_cache, v_cache, kind, cap, cache_len, max_len_hint,
+                         sink, o, B, 1, Hq, Hkv, dqk, dv, window, scale, num_splits, workspace,
+                         ws_bytes, dtype, stream, 1, 1, rope_dim, rope_base, nullptr);
+}
+
+int sinkattn_verify_rope(const void *q, const void *k_new, const void *v_new,
+                         const void *k_cache, const void *v_cache, int kind, int cap,
+                         const int32_t *cache_len, int max_len_hint, const float *sink, void *o,
+                         void *k_rot, int B, int nq, int Hq, int Hkv, int dqk, int dv,
+                         int window, float scale, int rope_dim, double rope_base,
+                         int num_splits, void *workspace, size_t ws_bytes, int dtype,
+                         void *stream) {
+    return cached_common(q, k_new, v_new, (void *)k_cache, (void *)v_cache, kind, cap,
+                         cache_len, max_len_hint, sink, o, B, nq, Hq, Hkv, dqk, dv, window,
+                         scale, num_splits, workspace, ws_bytes, dtype, stream, 0, 1, rope_dim,
+                         rope_base, k_rot);
 }
 
 int sinkattn_kv_append(const void *k_new, const void *v_new, void *k_cache, void *v_cache,

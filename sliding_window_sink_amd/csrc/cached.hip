@@ -41,6 +41,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKb = 32;
+constexpr int kMaxNq = 8;
 constexpr int kMergeStride = kDv + 4;  // floats per (wave, column): acc[128], m, l, pad
 constexpr uint32_t kOob = 0x80000000u;  // an offset past every descriptor: reads 0
 
@@ -71,9 +72,10 @@ struct KVRegs {
     uint2 v[16];         // keys 16*hh + i, dims 4r .. 4r+3
 };
 
-template <int NCB>
+template <int NCB, bool kRope>
 __global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, float scale_log2) {
     __shared__ __attribute__((aligned(16))) float merge[kWaves - 1][32][kMergeStride];
+    __shared__ float2 rope_tab[kRope ? kMaxNq * 32 : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 31, hh = lane >> 5;
     const int split = blockIdx.x % a.n_splits;
@@ -93,18 +95,28 @@ __global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, flo
     const BufRsrc kn = make_buf((const uint16_t *)a.k_new + nrow0 * kDqk, new_bytes_k);
     const BufRsrc vn = make_buf((const uint16_t *)a.v_new + nrow0 * kDv, new_bytes_v);
 
-    // Decode: store the new token into the cache (slot / index P).  Nothing in
-    // this launch reads that cache row.
-    if (a.write_new && split == 0 && (a.ring || c.P < a.cap)) {
-        const int slot = a.ring ? (c.P % a.cap) : c.P;
-        uint16_t *kd = (uint16_t *)a.k_cache + (crow0 + slot) * kDqk;
-        uint16_t *vd = (uint16_t *)a.v_cache + (crow0 + slot) * kDv;
-        const uint16_t *ks = (const uint16_t *)a.k_new + nrow0 * kDqk;
-        const uint16_t *vs = (const uint16_t *)a.v_new + nrow0 * kDv;
-        if (tid < kDqk / 8)
-            *(uint4 *)(kd + tid * 8) = *(const uint4 *)(ks + tid * 8);
-        else if (tid < kDqk / 8 + kDv / 8)
-            *(uint4 *)(vd + (tid - kDqk / 8) * 8) = *(const uint4 *)(vs + (tid - kDqk / 8) * 8);
+    // RoPE (when fused): (cos, sin) of positions P .. P+nq-1 for q and the new keys.
+    if constexpr (kRope) {
+        rope_fill_table64(rope_tab, c.P, nq, a.rope_base, tid, kThreads);
+        __syncthreads();
+    }
+    // Decode: store the new token into the cache (slot / index P); verify with
+    // fused RoPE: write the rotated new keys out.  Nothing in this launch reads
+    // those rows.
+    if (split == 0) {
+        if constexpr (kRope) {
+            cached_store_new<true>(a, crow0, nrow0, c.P, rope_tab, tid, kThreads);
+        } else if (a.write_new && (a.ring || c.P < a.cap)) {
+            const int slot = a.ring ? (c.P % a.cap) : c.P;
+            uint16_t *kd = (uint16_t *)a.k_cache + (crow0 + slot) * kDqk;
+            uint16_t *vd = (uint16_t *)a.v_cache + (crow0 + slot) * kDv;
+            const uint16_t *ks = (const uint16_t *)a.k_new + nrow0 * kDqk;
+            const uint16_t *vs = (const uint16_t *)a.v_new + nrow0 * kDv;
+            if (tid < kDqk / 8)
+                *(uint4 *)(kd + tid * 8) = *(const uint4 *)(ks + tid * 8);
+            else if (tid < kDqk / 8 + kDv / 8)
+                *(uint4 *)(vd + (tid - kDqk / 8) * 8) = *(const uint4 *)(vs + (tid - kDqk / 8) * 8);
+        }
     }
 
     // Q^T operands; column cb*32 + r is (token t, head) = divmod(column, group).
@@ -125,6 +137,12 @@ __global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, flo
 #pragma unroll
             for (int s = 0; s < kDqk / 16; ++s)
                 qf[cb][s] = as_bf16x8(buf_load16(qb, off + (uint32_t)s * 32));
+            if (kRope && ok) {  // dims 16s + 8hh .. +7 (s < 4): pairs 8s + 4hh ..
+                const float2 *cs = rope_tab + t * 32 + 4 * hh;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    qf[cb][s] = as_bf16x8(rope_chunk_bf16(as_uint4(qf[cb][s]), cs + 8 * s));
+            }
         }
     }
 
@@ -172,6 +190,12 @@ __global__ __launch_bounds__(kThreads) void cached_bf16_kernel(CachedArgs a, flo
 #pragma unroll
             for (int s = 0; s < kDqk / 16; ++s)
                 x.k[s] = buf_load16(kn, off + (uint32_t)s * 32);
+            if (kRope && p < c.rhi) {
+                const float2 *cs = rope_tab + (p - c.P) * 32 + 4 * hh;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    x.k[s] = rope_chunk_bf16(x.k[s], cs + 8 * s);
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int pv = kb + 16 * hh + i;
@@ -473,10 +497,17 @@ hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s) {
         const hipError_t e16 = launch_decode16(a, s);
         if (e16 != hipSuccess)
             return e16;
-    } else if (n_cols <= 32)
-        cached_bf16_kernel<1><<<grid, block, 0, s>>>(a, scale_log2);
-    else
-        cached_bf16_kernel<2><<<grid, block, 0, s>>>(a, scale_log2);
+    } else if (n_cols <= 32) {
+        if (a.rope)
+            cached_bf16_kernel<1, true><<<grid, block, 0, s>>>(a, scale_log2);
+        else
+            cached_bf16_kernel<1, false><<<grid, block, 0, s>>>(a, scale_log2);
+    } else {
+        if (a.rope)
+            cached_bf16_kernel<2, true><<<grid, block, 0, s>>>(a, scale_log2);
+        else
+            cached_bf16_kernel<2, false><<<grid, block, 0, s>>>(a, scale_log2);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_splits == 1)
         return e;

@@ -157,6 +157,13 @@ __device__ __forceinline__ void rope_pair(float x0, float x1, float2 cs, float &
     y0 = __fmaf_rn(x0, cs.x, -__fmul_rn(x1, cs.y));
     y1 = __fmaf_rn(x0, cs.y, __fmul_rn(x1, cs.x));
 }
+// (cos, sin) of the 32 pairs of a 64-dim rotation for positions pos0 .. pos0+n-1,
+// tab[t * 32 + c], filled cooperatively by the workgroup (the caller syncs).
+__device__ __forceinline__ void rope_fill_table64(float2 *tab, int pos0, int n, double base,
+                                                  int tid, int nthreads) {
+    for (int i = tid; i < n * 32; i += nthreads)
+        tab[i] = rope_cos_sin(pos0 + (i >> 5), rope_inv_freq(base, i & 31, 64));
+}
 // Rotate the 4 interleaved pairs held in 8 bf16 (one 16-byte chunk); cs[p] is the
 // (cos, sin) of pair p of the chunk.
 __device__ __forceinline__ uint4 rope_chunk_bf16(uint4 x, const float2 *cs) {
@@ -170,6 +177,44 @@ __device__ __forceinline__ uint4 rope_chunk_bf16(uint4 x, const float2 *cs) {
         w[p] = pack_bf16x2(y0, y1);
     }
     return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// New-token side effects of a decode / verify launch, done by one workgroup per
+// (sequence, KV head): decode stores token 0 into the cache at position P (its
+// k rotated when kRope); with kRope a k_rot output receives every new token's
+// rotated k.  tab holds the (cos, sin) of positions P .. P+nq-1 when kRope.  Nothing in
+// the launch reads the rows written here.
+template <bool kRope>
+__device__ __forceinline__ void cached_store_new(const CachedArgs &a, size_t crow0, size_t nrow0,
+                                                 int P, const float2 *tab, int tid,
+                                                 int nthreads) {
+    const uint16_t *ks = (const uint16_t *)a.k_new;
+    if (a.write_new && (a.ring || P < a.cap)) {
+        const int slot = a.ring ? (P % a.cap) : P;
+        uint16_t *kd = (uint16_t *)a.k_cache + (crow0 + slot) * kDqk;
+        uint16_t *vd = (uint16_t *)a.v_cache + (crow0 + slot) * kDv;
+        const uint16_t *vs = (const uint16_t *)a.v_new + nrow0 * kDv;
+        for (int i = tid; i < (kDqk + kDv) / 8; i += nthreads) {
+            if (i < kDqk / 8) {
+                uint4 x = *(const uint4 *)(ks + nrow0 * kDqk + i * 8);
+                if (kRope && i < 8)
+                    x = rope_chunk_bf16(x, tab + 4 * i);
+                *(uint4 *)(kd + i * 8) = x;
+            } else {
+                *(uint4 *)(vd + (i - kDqk / 8) * 8) = *(const uint4 *)(vs + (i - kDqk / 8) * 8);
+            }
+        }
+    }
+    if (kRope && a.k_rot) {
+        for (int i = tid; i < a.nq * (kDqk / 8); i += nthreads) {
+            const int t = i / (kDqk / 8), ci = i % (kDqk / 8);
+            const size_t row = nrow0 + (size_t)t * a.Hkv;
+            uint4 x = *(const uint4 *)(ks + row * kDqk + ci * 8);
+            if (ci < 8)
+                x = rope_chunk_bf16(x, tab + t * 32 + 4 * ci);
+            *(uint4 *)((uint16_t *)a.k_rot + row * kDqk + ci * 8) = x;
+        }
+    }
 }
 
 }  // namespace sinkattn

@@ -37,6 +37,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kKb = 32;
 constexpr int kCols = 16;
+constexpr int kMaxNq = kCols / 8;  // at least 8 query heads per KV head
 constexpr int kMergeStride = kDv + 4;
 constexpr uint32_t kOob = 0x80000000u;  // an offset past every descriptor: reads 0
 
@@ -51,6 +52,7 @@ struct KV16 {
 
 __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, float scale_log2) {
     __shared__ __attribute__((aligned(16))) float merge[kWaves - 1][kCols][kMergeStride];
+    __shared__ float2 rope_tab[kMaxNq * 32];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, kg = lane >> 4;
@@ -72,20 +74,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     const size_t crow0 = ((size_t)b * Hkv + g) * a.cap;
     const size_t nrow0 = (size_t)b * nq * Hkv + g;  // row of new token t: nrow0 + t*Hkv
 
-    // Decode: the chunk holding position P stores the new token (slot / index P).
-    if (a.write_new && P >= rlo && P < rhi && (a.ring || P < a.cap)) {
-        const int slot = a.ring ? (P % a.cap) : P;
-        uint16_t *kd = (uint16_t *)a.k_cache + (crow0 + slot) * kDqk;
-        uint16_t *vd = (uint16_t *)a.v_cache + (crow0 + slot) * kDv;
-        const uint16_t *ks = (const uint16_t *)a.k_new + nrow0 * kDqk;
-        const uint16_t *vs = (const uint16_t *)a.v_new + nrow0 * kDv;
-        if (tid < kDqk / 8)
-            *(uint4 *)(kd + tid * 8) = *(const uint4 *)(ks + tid * 8);
-        else if (tid < kDqk / 8 + kDv / 8)
-            *(uint4 *)(vd + (tid - kDqk / 8) * 8) = *(const uint4 *)(vs + (tid - kDqk / 8) * 8);
-    }
     if (rlo >= rhi)
         return;  // uniform: this chunk holds no visible key
+
+    // RoPE (when fused): (cos, sin) of positions P .. P+nq-1 for q and the new keys.
+    if (a.rope) {
+        rope_fill_table64(rope_tab, P, nq, a.rope_base, tid, kThreads);
+        __syncthreads();
+    }
+    // The chunk holding position P stores the new token (decode) / rotated keys.
+    if (P >= rlo && P < rhi) {
+        if (a.rope)
+            cached_store_new<true>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
+        else
+            cached_store_new<false>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
+    }
 
     const uint64_t cache_rows = a.ring ? (uint64_t)a.cap : (uint64_t)P;
     const BufRsrc kc = make_buf((const uint16_t *)a.k_cache + crow0 * kDqk, cache_rows * kDqk * 2);
@@ -105,9 +108,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
         const uint32_t off =
             col_ok ? ((uint32_t)((lr / group) * Hq + g * group + lr % group) * kDqk + (uint32_t)kg * 8) * 2
                    : kOob;
+        uint4 qr[kDqk / 32];
 #pragma unroll
         for (int s = 0; s < kDqk / 32; ++s)
-            qf[s] = as_bf16x8(buf_load16(qb, off + (uint32_t)s * 64));
+            qr[s] = buf_load16(qb, off + (uint32_t)s * 64);
+        if (a.rope && col_ok) {  // dims 32s + 8kg .. +7 (s < 2): pairs 16s + 4kg ..
+            const float2 *cs = rope_tab + (lr / group) * 32 + 4 * kg;
+            qr[0] = rope_chunk_bf16(qr[0], cs);
+            qr[1] = rope_chunk_bf16(qr[1], cs + 16);
+        }
+#pragma unroll
+        for (int s = 0; s < kDqk / 32; ++s)
+            qf[s] = as_bf16x8(qr[s]);
     }
 
     float m = -INFINITY, l = 0.f;
@@ -159,6 +171,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
 #pragma unroll
             for (int s = 0; s < kDqk / 32; ++s)
                 x.k[kt][s] = buf_load16(kn, off + (uint32_t)s * 64);
+            if (a.rope && p < rhi) {
+                const float2 *cs = rope_tab + (p - P) * 32 + 4 * kg;
+                x.k[kt][0] = rope_chunk_bf16(x.k[kt][0], cs);
+                x.k[kt][1] = rope_chunk_bf16(x.k[kt][1], cs + 16);
+            }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {

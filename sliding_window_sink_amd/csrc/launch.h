@@ -1,5 +1,5 @@
 // launch.h -- internal parameter blocks and launchers (host <-> kernels).
-// Nothing here crosses the public C ABI; the host entry points in api.cpp
+// Nothing here crosses the public C ABI; the host entry points in api.hip
 // validate arguments and then call these launchers on the caller's stream.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -15,6 +15,8 @@ struct PrefillArgs {
     float *lse;             // [B,Hq,T] or nullptr
     int B, T, Hq, Hkv, window;
     float scale;            // softmax scale (natural units)
+    int rope_q = 0;         // global bf16 kernel: rotate q (64 dims, interleaved) on load
+    double rope_base = 0.0;
 };
 
 // Queries at positions cache_len[b] + t (t < nq) over a ring or contiguous
@@ -31,6 +33,9 @@ struct CachedArgs {
     int max_len;                // cache_len values are clamped to [0, max_len]
     int n_splits, chunk;        // context chunks (chunk keys each) when n_splits > 1
     float scale;
+    int rope;                   // rotate q and k_new (64 dims, interleaved) at P + t
+    double rope_base;
+    void *k_rot;                // [B,nq,Hkv,192]: rotated k_new out, or nullptr
 };
 
 struct AppendArgs {
@@ -45,6 +50,10 @@ __device__ __forceinline__ int clamp_len(int len, int max_len) {
     return len < 0 ? 0 : (len > max_len ? max_len : len);
 }
 
+// Out-of-place partial RoPE of bf16 rows [B,T,H,192] at positions 0..T-1 of
+// each sequence (64 dims, interleaved pairs; dims 64.. copied).
+hipError_t launch_rope_rows(const void *src, void *dst, int B, int T, int n_heads, double base,
+                            hipStream_t s);
 hipError_t launch_rope(void *x, int bf16, int64_t n_tok, int n_heads, int head_dim, int rope_dim,
                        const int32_t *pos, double base, int style, hipStream_t s);
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);

@@ -67,10 +67,11 @@ struct Staged {
     uint4 v;
 };
 
-template <bool kWindowed>
+template <bool kWindowed, bool kRopeQ>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, int n_units,
                                                                  int n_tiles, float scale_log2) {
     __shared__ PrefillSmem sm;
+    __shared__ float2 rope_tab[kRopeQ ? kTq * 32 : 1];
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, window = a.window;
     const int group = Hq / Hkv;
     const int parts = group / kWaves;
@@ -97,6 +98,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
     const BufRsrc obuf = make_buf((uint16_t *)a.o + row0 * Hq * kDv, (uint64_t)T * orow);
     const uint32_t kcol = (uint32_t)g * kDqk * 2, vcol = (uint32_t)g * kDv * 2;
 
+    // Partial RoPE of q on load (fused variant): (cos, sin) of the tile's 32
+    // positions, computed once per workgroup.
+    if constexpr (kRopeQ) {
+        rope_fill_table64(rope_tab, t0, kTq, a.rope_base, tid, kThreads);
+        __syncthreads();
+    }
+
     // Q^T as the B operand: k-step s, lane half hh -> head dims (2s+hh)*8 .. +7.
     uint4 qf[kDqk / 16];
     {
@@ -104,6 +112,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
 #pragma unroll
         for (int s = 0; s < kDqk / 16; ++s)
             qf[s] = buf_load16(qbuf, off + (uint32_t)s * 32);
+        if constexpr (kRopeQ) {  // dims 16s + 8hh .. +7 (s < 4): pairs 8s + 4hh ..
+            const float2 *cs = rope_tab + r * 32 + 4 * hh;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                qf[s] = rope_chunk_bf16(qf[s], cs + 8 * s);
+        }
     }
 
     const int kstart = kWindowed ? max(0, t0 - window + 1) : 0;
@@ -270,9 +284,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 grid((unsigned)(n_units * n_tiles)), block(kThreads);
     if (a.window > 0)
-        prefill_bf16_kernel<true><<<grid, block, 0, s>>>(a, n_units, n_tiles, scale_log2);
+        prefill_bf16_kernel<true, false><<<grid, block, 0, s>>>(a, n_units, n_tiles, scale_log2);
+    else if (a.rope_q)
+        prefill_bf16_kernel<false, true><<<grid, block, 0, s>>>(a, n_units, n_tiles, scale_log2);
     else
-        prefill_bf16_kernel<false><<<grid, block, 0, s>>>(a, n_units, n_tiles, scale_log2);
+        prefill_bf16_kernel<false, false><<<grid, block, 0, s>>>(a, n_units, n_tiles, scale_log2);
     return hipGetLastError();
 }
 

@@ -61,7 +61,43 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T *x, int64_t n_tok, int
     }
 }
 
+// Out-of-place variant for bf16 rows of 192 dims at positions 0..T-1 of each
+// sequence (the keys of a prefill with the RoPE fused): one thread per 16-byte
+// chunk; chunks 0..7 (dims 0..63, interleaved pairs) are rotated with the same
+// cos/sin and rounding as rope_kernel, the rest are copied.
+__global__ __launch_bounds__(kThreads) void rope_rows_kernel(const uint4 *src, uint4 *dst,
+                                                             int64_t n_tok, int T, int n_heads,
+                                                             double base) {
+    __shared__ float2 cs[kTokens * 32];
+    const int64_t tok0 = (int64_t)blockIdx.x * kTokens;
+    const int ntok = (int)min<int64_t>(kTokens, n_tok - tok0);
+    for (int idx = threadIdx.x; idx < ntok * 32; idx += kThreads)
+        cs[idx] = rope_cos_sin((int)((tok0 + (idx >> 5)) % T), rope_inv_freq(base, idx & 31, 64));
+    __syncthreads();
+    constexpr int kChunks = kDqk / 8;
+    const int per_tok = n_heads * kChunks;
+    for (int idx = threadIdx.x; idx < ntok * per_tok; idx += kThreads) {
+        const int tt = idx / per_tok, ci = (idx % per_tok) % kChunks;
+        const int64_t at = tok0 * per_tok + idx;
+        uint4 x = src[at];
+        if (ci < 8)
+            x = rope_chunk_bf16(x, cs + tt * 32 + 4 * ci);
+        dst[at] = x;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_rope_rows(const void *src, void *dst, int B, int T, int n_heads, double base,
+                            hipStream_t s) {
+    const int64_t n_tok = (int64_t)B * T;
+    if (n_tok == 0 || n_heads == 0)
+        return hipSuccess;
+    const unsigned blocks = (unsigned)((n_tok + kTokens - 1) / kTokens);
+    rope_rows_kernel<<<dim3(blocks), dim3(kThreads), 0, s>>>((const uint4 *)src, (uint4 *)dst,
+                                                             n_tok, T, n_heads, base);
+    return hipGetLastError();
+}
 
 hipError_t launch_rope(void *x, int bf16, int64_t n_tok, int n_heads, int head_dim, int rope_dim,
                        const int32_t *pos, double base, int style, hipStream_t s) {

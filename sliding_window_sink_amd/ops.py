@@ -60,6 +60,12 @@ def _bind(lib):
         "sinkattn_verify": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32, i32,
                              i32, f32, i32, p, sz, i32, p], i32),
         "sinkattn_kv_append": ([p, p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, i32, p], i32),
+        "sinkattn_prefill_global_rope": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32,
+                                          i32, f64, i32, p], i32),
+        "sinkattn_decode_rope": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32,
+                                  i32, f32, i32, f64, i32, p, sz, i32, p], i32),
+        "sinkattn_verify_rope": ([p, p, p, p, p, i32, i32, p, i32, p, p, p, i32, i32, i32, i32,
+                                  i32, i32, i32, f32, i32, f64, i32, p, sz, i32, p], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -84,7 +90,8 @@ def lib():
 
 EXPORTED = ["sinkattn_abi_version", "sinkattn_status_string", "sinkattn_rope_partial",
             "sinkattn_prefill_swa", "sinkattn_prefill_swa_rope", "sinkattn_prefill_global", "sinkattn_decode_workspace_bytes",
-            "sinkattn_decode", "sinkattn_verify", "sinkattn_kv_append"]
+            "sinkattn_decode", "sinkattn_verify", "sinkattn_kv_append",
+            "sinkattn_prefill_global_rope", "sinkattn_decode_rope", "sinkattn_verify_rope"]
 
 
 def _check(rc: int):
@@ -191,13 +198,36 @@ def prefill_global(q, k, v, sink, scale=None, out=None, return_lse=False):
     return _prefill("sinkattn_prefill_global", q, k, v, sink, 0, scale, out, return_lse)
 
 
+def prefill_global_rope(q, k, v, sink, base: float = 5e6, rope_dim: int = 64, k_rot=None,
+                        scale=None, out=None, return_lse=False):
+    """Global prefill with partial RoPE fused (q, k un-rotated and left untouched).
+    The rotated keys are written to k_rot (allocated here when not given), which
+    is returned as the second element: (o, k_rot) or (o, lse, k_rot)."""
+    _dev(q, k, v, sink, out, k_rot)
+    B, T, Hq, dqk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    if k.shape != (B, T, Hkv, dqk) or v.shape[:3] != (B, T, Hkv) or sink.shape != (Hq,):
+        raise SinkAttnError(-2, "q/k/v/sink shapes disagree")
+    if k_rot is None:
+        k_rot = torch.empty_like(k)
+    if k_rot.shape != k.shape or k_rot.dtype != k.dtype:
+        raise SinkAttnError(-2, "k_rot must match k")
+    o = out if out is not None else torch.empty((B, T, Hq, dv), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib().sinkattn_prefill_global_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o),
+                                              _ptr(lse), _ptr(k_rot), B, T, Hq, Hkv, dqk, dv,
+                                              _scale(scale), int(rope_dim), float(base),
+                                              _dtype_code(q), _stream()))
+    return (o, lse, k_rot) if return_lse else (o, k_rot)
+
+
 def decode_workspace_bytes(B: int, Hq: int, n_q: int = 1, max_splits: int = 64, dv: int = DV) -> int:
     return int(lib().sinkattn_decode_workspace_bytes(B, Hq, dv, n_q, max_splits))
 
 
 def _cached(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window, max_len_hint,
-            num_splits, workspace, scale, out, verify):
-    _dev(q, k_new, v_new, k_cache, v_cache, cache_len, sink, workspace, out)
+            num_splits, workspace, scale, out, verify, rope=None, k_rot=None):
+    _dev(q, k_new, v_new, k_cache, v_cache, cache_len, sink, workspace, out, k_rot)
     if cache_len.dtype != torch.int32:
         raise SinkAttnError(-3, "cache_len must be int32")
     if verify:
@@ -217,13 +247,23 @@ def _cached(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window, ma
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    if k_rot is not None and (k_rot.shape != k_new.shape or k_rot.dtype != k_new.dtype):
+        raise SinkAttnError(-2, "k_rot must match k_new")
     args = [_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), int(kind), cap,
-            _ptr(cache_len), int(max_len_hint), _ptr(sink), _ptr(o), B]
+            _ptr(cache_len), int(max_len_hint), _ptr(sink), _ptr(o)]
+    if verify and rope is not None:
+        args.append(_ptr(k_rot))
+    args.append(B)
     if verify:
         args.append(nq)
-    args += [Hq, Hkv, dqk, dv, int(window), _scale(scale), int(num_splits), ws_ptr, ws_bytes,
-             _dtype_code(q), _stream()]
-    fn = lib().sinkattn_verify if verify else lib().sinkattn_decode
+    args += [Hq, Hkv, dqk, dv, int(window), _scale(scale)]
+    if rope is not None:
+        args += [int(rope[1]), float(rope[0])]
+    args += [int(num_splits), ws_ptr, ws_bytes, _dtype_code(q), _stream()]
+    if rope is None:
+        fn = lib().sinkattn_verify if verify else lib().sinkattn_decode
+    else:
+        fn = lib().sinkattn_verify_rope if verify else lib().sinkattn_decode_rope
     _check(fn(*args))
     return o
 
@@ -244,6 +284,29 @@ def verify(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind=RING, window
         raise SinkAttnError(-2, "max_len_hint (host bound on cache_len) is required")
     return _cached(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window, max_len_hint,
                    num_splits, workspace, scale, out, verify=True)
+
+
+def decode_rope(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind=RING, window=128,
+                max_len_hint=None, base: float = 1e4, rope_dim: int = 64, num_splits=0,
+                workspace=None, scale=None, out=None):
+    """decode() with partial RoPE fused: q and k_new are un-rotated; the token is
+    rotated at position cache_len[b] and its rotated k is stored in the cache."""
+    if max_len_hint is None:
+        raise SinkAttnError(-2, "max_len_hint (host bound on cache_len) is required")
+    return _cached(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window, max_len_hint,
+                   num_splits, workspace, scale, out, verify=False, rope=(base, rope_dim))
+
+
+def verify_rope(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind=RING, window=128,
+                max_len_hint=None, base: float = 1e4, rope_dim: int = 64, k_rot=None,
+                num_splits=0, workspace=None, scale=None, out=None):
+    """verify() with partial RoPE fused: token t rotated at cache_len[b] + t; if
+    k_rot is given it receives the rotated k_new (for a later kv_append)."""
+    if max_len_hint is None:
+        raise SinkAttnError(-2, "max_len_hint (host bound on cache_len) is required")
+    return _cached(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window, max_len_hint,
+                   num_splits, workspace, scale, out, verify=True, rope=(base, rope_dim),
+                   k_rot=k_rot)
 
 
 def kv_append(k_new, v_new, k_cache, v_cache, cache_len, kind=RING, n_accept=None):

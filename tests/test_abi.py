@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 10, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(ops.EXPORTED) == names
@@ -124,6 +124,43 @@ def test_prefill_swa_rope_validation(lib):
     assert call(window=0) == SHAPE
     assert call(k_rot=P(FAKE[1].value + 128)) == ALIAS   # k_rot over k
     assert call(Hq=15) == SHAPE           # Hq % Hkv != 0
+
+
+def test_prefill_global_rope_validation(lib):
+    f = lib.sinkattn_prefill_global_rope
+    def call(rope_dim=64, dtype=1, base=5e6, k_rot=FAKE[7], Hq=16, B=1, T=64, o=FAKE[4]):
+        return f(FAKE[0], FAKE[1], FAKE[2], FAKE[3], o, None, k_rot, B, T, Hq, 2, 192, 128, 0.0,
+                 rope_dim, base, dtype, None)
+    assert call(k_rot=None) == NULL                 # the attention reads k_rot back
+    assert call(rope_dim=32) == UNSUP
+    assert call(dtype=0) == UNSUP
+    assert call(rope_dim=63) == SHAPE
+    assert call(base=float("inf")) == SHAPE
+    assert call(Hq=15) == SHAPE
+    assert call(k_rot=P(FAKE[1].value + 64)) == ALIAS   # k_rot over k
+    assert call(k_rot=P(FAKE[4].value + 64)) == ALIAS   # k_rot over o
+    assert call(B=0) == OK
+
+
+def test_decode_verify_rope_validation(lib):
+    def dec(rope_dim=64, base=1e4, dtype=1, B=2):
+        return lib.sinkattn_decode_rope(FAKE[0], FAKE[1], FAKE[2], FAKE[3], P(13 << 36), 0, 128,
+                                        FAKE[5], 1000, FAKE[6], FAKE[9], B, 16, 2, 192, 128, 128,
+                                        0.0, rope_dim, base, 0, None, 0, dtype, None)
+    assert dec(rope_dim=32) == UNSUP
+    assert dec(dtype=0) == UNSUP
+    assert dec(rope_dim=7) == SHAPE
+    assert dec(base=-1.0) == SHAPE
+    assert dec(B=0) == OK
+
+    def ver(k_rot=None, rope_dim=64, nq=4):
+        return lib.sinkattn_verify_rope(FAKE[0], FAKE[1], FAKE[2], FAKE[3], P(13 << 36), 0, 128,
+                                        FAKE[5], 1000, FAKE[6], FAKE[9], k_rot, 2, nq, 16, 2, 192,
+                                        128, 128, 0.0, rope_dim, 1e4, 0, None, 0, 1, None)
+    assert ver(rope_dim=128) == UNSUP
+    assert ver(nq=9) == SHAPE
+    assert ver(k_rot=P(FAKE[1].value + 32)) == ALIAS   # k_rot over k_new
+    assert ver(k_rot=P(FAKE[9].value + 32)) == ALIAS   # k_rot over o
 
 
 def test_rope_and_append_validation(lib):
