@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--prewarm-s", type=float, default=1.0,
                    help="untimed seconds of steps before the warm-up steps (clock ramp)")
-    p.add_argument("--only", default="", help="comma list of: swa,global,decode,verify")
+    p.add_argument("--only", default="", help="comma list of: swa,global,decode,verify,spec")
     p.add_argument("--counter-pass", action="store_true",
                    help="for rocprofv3 --pmc runs: one 1 GiB device copy (the calibration "
                         "kernel of known traffic), then 3 launches of the headline kernel")
@@ -406,6 +406,108 @@ def run_verify(torch, ops, synth, dev):
                 kv_gbs=(kv_s + kv_g) / step_ms / 1e6)
 
 
+def run_spec_loop(torch, ops, synth, dev, reps=20):
+    """Kernel-level self-speculative step at the batch-64 / 16K-context workload:
+    3 MTP draft SWA decodes (ring, W=128), then for each of the 5 SWA + 1 global
+    layers a verify of 1 + 3 tokens (RoPE fused, rotated keys out) and a
+    kv_append of the accepted tokens, then advance_len -- against one plain
+    decode step of the same 6 layers.  Acceptance is taken as 4 of 4 (the most
+    commit traffic).  The attention-level speed-up at acceptance length a is
+    a * decode_step / spec_step."""
+    w = synth.WORKLOADS[5]
+    B, nq, Hq, L = w.B, w.T, 64, 16384
+    cap = L + 8 + nq * 4
+    cl0 = torch.full((B,), L, dtype=torch.int32, device=dev)
+    cl_d = cl0.clone()
+    n_acc = torch.full((B,), nq, dtype=torch.int32, device=dev)
+    s0 = w.seed * 1000
+
+    def ring_layer(seed, n_tok):
+        return dict(q=synth.device_normal(seed, (B, n_tok, Hq, 192), device=dev),
+                    kn=synth.device_normal(seed + 1, (B, n_tok, 8, 192), device=dev),
+                    vn=synth.device_normal(seed + 2, (B, n_tok, 8, 128), device=dev),
+                    kc=synth.device_normal(seed + 3, (B, 8, 128, 192), device=dev),
+                    vc=synth.device_normal(seed + 4, (B, 8, 128, 128), device=dev),
+                    sink=synth.device_normal(seed + 5, (Hq,), torch.float32, device=dev),
+                    o=torch.empty(B, n_tok, Hq, 128, dtype=torch.bfloat16, device=dev),
+                    kind=ops.RING, window=128, base=synth.BASE_SWA)
+
+    layers = [ring_layer(s0 + 10 * i, nq) for i in range(5)]
+    gl = dict(q=synth.device_normal(s0 + 60, (B, nq, Hq, 192), device=dev),
+              kn=synth.device_normal(s0 + 61, (B, nq, 4, 192), device=dev),
+              vn=synth.device_normal(s0 + 62, (B, nq, 4, 128), device=dev),
+              kc=torch.empty(B, 4, cap, 192, dtype=torch.bfloat16, device=dev),
+              vc=torch.empty(B, 4, cap, 128, dtype=torch.bfloat16, device=dev),
+              sink=synth.device_normal(s0 + 65, (Hq,), torch.float32, device=dev),
+              o=torch.empty(B, nq, Hq, 128, dtype=torch.bfloat16, device=dev),
+              kind=ops.CONTIG, window=0, base=synth.BASE_GA)
+    synth.device_normal(s0 + 63, None, device=dev, out=gl["kc"][:, :, :L])
+    synth.device_normal(s0 + 64, None, device=dev, out=gl["vc"][:, :, :L])
+    layers.append(gl)
+    drafts = [ring_layer(s0 + 100 + 10 * i, 1) for i in range(3)]
+    for d in layers + drafts:
+        d["k_rot"] = torch.empty_like(d["kn"])
+    ws = torch.empty(ops.decode_workspace_bytes(B, Hq, nq, 256) // 4, dtype=torch.float32,
+                     device=dev)
+    hint = L + nq  # host bound on cache_len within one step
+
+    def spec_step():
+        for d in drafts:
+            dec(d)
+        for d in layers:
+            ops.verify_rope(d["q"], d["kn"], d["vn"], d["kc"], d["vc"], cl_d, d["sink"],
+                            d["kind"], d["window"], hint, base=d["base"], k_rot=d["k_rot"],
+                            num_splits=0, workspace=ws, out=d["o"])
+            ops.kv_append(d["k_rot"], d["vn"], d["kc"], d["vc"], cl_d, d["kind"], n_acc)
+        ops.advance_len(cl_d, nq, n_acc)
+
+    def decode_step():
+        for d in layers:
+            dec(d)
+
+    # a decode reads one token: contiguous [B, ...] copies of token 0
+    for d in layers + drafts:
+        for key in ("q", "kn", "vn", "o"):
+            d[key + "0"] = d[key][:, 0].contiguous()
+
+    def dec(d):
+        ops.decode_rope(d["q0"], d["kn0"], d["vn0"], d["kc"], d["vc"], cl_d, d["sink"],
+                        d["kind"], d["window"], hint, base=d["base"], num_splits=0,
+                        workspace=ws, out=d["o0"])
+
+    def graph_of(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+            cl_d.copy_(cl0)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        cl_d.copy_(cl0)
+        torch.cuda.synchronize()
+        return gr
+
+    g_spec, g_dec = graph_of(spec_step), graph_of(decode_step)
+    t_spec, t_dec = Timer(torch), Timer(torch)
+    for _ in range(reps):
+        cl_d.copy_(cl0)  # each timed step starts from the same lengths
+        with t_spec:
+            g_spec.replay()
+        cl_d.copy_(cl0)
+        with t_dec:
+            g_dec.replay()
+    torch.cuda.synchronize()
+    spec_ms, dec_ms = t_spec.mean_ms(), t_dec.mean_ms()
+    del layers, drafts, gl
+    return dict(workload="spec_loop_bf16_B64_ctx16384_3draft_5swa+1ga_nq4", spec_step_ms=spec_ms,
+                decode_step_ms=dec_ms, spec_over_decode=spec_ms / dec_ms,
+                attn_speedup_at_accept={str(a): round(a * dec_ms / spec_ms, 3)
+                                        for a in (2.8, 3.0, 3.2, 3.4, 3.6, 3.8)})
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(torch, inputs, target_s: float):
@@ -466,7 +568,8 @@ def main():
     ops.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    only = set(args.only.split(",")) if args.only else {"swa", "global", "decode", "verify"}
+    only = set(args.only.split(",")) if args.only else {"swa", "global", "decode", "verify",
+                                                                "spec"}
 
     if args.counter_pass:
         # calibration: a plain copy moves exactly 1 GiB in and 1 GiB out
@@ -524,6 +627,9 @@ def main():
         if "decode" in only:
             log("[bench] hybrid-block decode B=32")
             others["hybrid_decode"] = run_hybrid_decode(torch, ops, synth, dev)
+        if "spec" in only:
+            log("[bench] self-speculative step B=64 ctx 16384")
+            others["spec_loop"] = run_spec_loop(torch, ops, synth, dev)
         if "verify" in only:
             log("[bench] speculative verify B=64 nq=4")
             others["verify"] = run_verify(torch, ops, synth, dev)

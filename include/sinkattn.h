@@ -233,6 +233,19 @@ int sinkattn_kv_append(const void *k_new, const void *v_new, void *k_cache, void
                        int kind, int cap, const int32_t *cache_len, const int32_t *n_accept,
                        int B, int n, int Hkv, int dqk, int dv, int dtype, void *stream);
 
+/*
+ * Advance the cached lengths after a commit (Section 2.3.1: accepted draft
+ * tokens join the context): cache_len[b] += min(max(n_accept[b], 0), n), or
+ * += n when n_accept is NULL -- exactly the tokens sinkattn_kv_append stored
+ * with the same n_accept and n.  cache_len and n_accept are device int32 [B];
+ * the update is stream-ordered, so a draft -> verify -> kv_append -> advance
+ * loop runs without any host round trip (the host keeps max_len_hint an upper
+ * bound by adding n per step).  Errors: NULL cache_len -> NULL_PTR; B < 0 or
+ * n < 0 -> SHAPE; cache_len overlapping n_accept -> ALIAS.
+ */
+int sinkattn_advance_len(int32_t *cache_len, const int32_t *n_accept, int B, int n,
+                         void *stream);
+
 #ifdef __cplusplus
 }
 #endif

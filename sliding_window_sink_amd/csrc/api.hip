@@ -441,4 +441,15 @@ int sinkattn_kv_append(const void *k_new, const void *v_new, void *k_cache, void
     return status_from_hip(launch_append(a, dtype == SINKATTN_BF16, (hipStream_t)stream));
 }
 
+int sinkattn_advance_len(int32_t *cache_len, const int32_t *n_accept, int B, int n,
+                         void *stream) {
+    if (!cache_len)
+        return SINKATTN_ERR_NULL_PTR;
+    if (B < 0 || n < 0)
+        return SINKATTN_ERR_SHAPE;
+    if (overlaps(cache_len, (size_t)B * 4, n_accept, n_accept ? (size_t)B * 4 : 0))
+        return SINKATTN_ERR_ALIAS;
+    return status_from_hip(launch_advance_len(cache_len, n_accept, B, n, (hipStream_t)stream));
+}
+
 }  // extern "C"

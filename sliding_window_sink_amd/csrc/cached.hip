@@ -445,6 +445,13 @@ __global__ __launch_bounds__(64) void combine_kernel(CachedArgs a, int out_bf16)
     }
 }
 
+// After a commit: cache_len[b] += the number of tokens kv_append stored for b.
+__global__ void advance_len_kernel(int32_t *cache_len, const int32_t *n_accept, int B, int n) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B)
+        cache_len[b] += n_accept ? min(n, max(0, n_accept[b])) : n;
+}
+
 // Commit accepted tokens: one thread per 16-byte piece of a K or V row.
 __global__ void append_kernel(AppendArgs a, int row_bytes_k, int row_bytes_v) {
     const int pk = row_bytes_k / 16, pv = row_bytes_v / 16;
@@ -493,7 +500,11 @@ hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s) {
     const int n_cols = a.nq * (a.Hq / a.Hkv);
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 grid((unsigned)(a.B * a.Hkv * a.n_splits)), block(kThreads);
-    if (n_cols <= 16) {
+    // <= 16 columns, or a short window (each workgroup's key range is a few
+    // blocks, so streaming it once per 16-column wave costs little): the
+    // 16-column kernel; long ranges with more columns: the 32-column kernel,
+    // whose waves split the key blocks.
+    if (n_cols <= 16 || (a.window > 0 && a.window <= 4096)) {
         const hipError_t e16 = launch_decode16(a, s);
         if (e16 != hipSuccess)
             return e16;
@@ -523,6 +534,15 @@ hipError_t launch_append(const AppendArgs &a, int bf16, hipStream_t s) {
         return hipSuccess;
     const unsigned blocks = (unsigned)((total + 255) / 256);
     append_kernel<<<dim3(blocks), dim3(256), 0, s>>>(a, rbk, rbv);
+    return hipGetLastError();
+}
+
+hipError_t launch_advance_len(int32_t *cache_len, const int32_t *n_accept, int B, int n,
+                              hipStream_t s) {
+    if (B == 0)
+        return hipSuccess;
+    advance_len_kernel<<<dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s>>>(cache_len,
+                                                                              n_accept, B, n);
     return hipGetLastError();
 }
 

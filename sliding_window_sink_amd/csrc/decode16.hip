@@ -4,7 +4,10 @@
 // sink softmax; Section 2.3.1 one new token per step over a per-request
 // cache), for the case where the (token, head) columns of one KV group number
 // at most 16: a decode step of a global layer (16 query heads per KV head,
-// Table 1) or of an SWA layer (8), or a 2-token verify of an SWA layer.
+// Table 1) or of an SWA layer (8), or a 2-token verify of an SWA layer.  A
+// second mode ("token waves") serves up to 64 columns over a short window
+// (verify of 1 + 3 tokens on an SWA layer): each wave takes 16 columns and
+// reads the whole key range, which for a 128-key window is only a few blocks.
 //
 // Why a second kernel: decode is HBM bound (16 FLOP per byte), and with only
 // 16 columns the 32x32 MFMA tile of cached.hip wastes half its columns and,
@@ -38,6 +41,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kKb = 32;
 constexpr int kCols = 16;
 constexpr int kMaxNq = kCols / 8;  // at least 8 query heads per KV head
+constexpr int kMaxNqTok = 4 * kCols / 8;
 constexpr int kMergeStride = kDv + 4;
 constexpr uint32_t kOob = 0x80000000u;  // an offset past every descriptor: reads 0
 
@@ -50,9 +54,14 @@ struct KV16 {
     uint4 v[8];             // key (e/4)*16 + 4(l/16) + e%4, dims 8(l%16) .. +7
 };
 
+template <bool kTok>
 __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, float scale_log2) {
-    __shared__ __attribute__((aligned(16))) float merge[kWaves - 1][kCols][kMergeStride];
-    __shared__ float2 rope_tab[kMaxNq * 32];
+    // kTok = false: <= 16 columns, the waves split the key blocks and merge.
+    // kTok = true: <= 64 columns, wave w owns columns 16w .. 16w+15 and reads
+    // every key block (the 4 waves stream the same rows: one HBM read, L2 hits).
+    constexpr int kMerge = kTok ? 0 : kWaves - 1;
+    __shared__ __attribute__((aligned(16))) float merge[kTok ? 1 : kMerge][kCols][kMergeStride];
+    __shared__ float2 rope_tab[(kTok ? kMaxNqTok : kMaxNq) * 32];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, kg = lane >> 4;
@@ -98,22 +107,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     const BufRsrc vn = make_buf((const uint16_t *)a.v_new + nrow0 * kDv,
                                 ((uint64_t)(nq - 1) * Hkv + 1) * kDv * 2);
 
-    // Q^T operand (B of the QK MFMA): column lr = (token t, head) = divmod(lr, group).
-    const bool col_ok = lr < n_cols;
-    const int qpos = col_ok ? P + lr / group : -1;
+    // Q^T operand (B of the QK MFMA): column col = (token t, head) = divmod(col, group).
+    const int col = kTok ? kCols * wave + lr : lr;
+    const bool col_ok = col < n_cols;
+    const int qpos = col_ok ? P + col / group : -1;
     bf16x8 qf[kDqk / 32];
     {
         const BufRsrc qb = make_buf((const uint16_t *)a.q + (size_t)b * nq * Hq * kDqk,
                                     (uint64_t)nq * Hq * kDqk * 2);
         const uint32_t off =
-            col_ok ? ((uint32_t)((lr / group) * Hq + g * group + lr % group) * kDqk + (uint32_t)kg * 8) * 2
+            col_ok ? ((uint32_t)((col / group) * Hq + g * group + col % group) * kDqk + (uint32_t)kg * 8) * 2
                    : kOob;
         uint4 qr[kDqk / 32];
 #pragma unroll
         for (int s = 0; s < kDqk / 32; ++s)
             qr[s] = buf_load16(qb, off + (uint32_t)s * 64);
         if (a.rope && col_ok) {  // dims 32s + 8kg .. +7 (s < 2): pairs 16s + 4kg ..
-            const float2 *cs = rope_tab + (lr / group) * 32 + 4 * kg;
+            const float2 *cs = rope_tab + (col / group) * 32 + 4 * kg;
             qr[0] = rope_chunk_bf16(qr[0], cs);
             qr[1] = rope_chunk_bf16(qr[1], cs + 16);
         }
@@ -259,7 +269,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // n_cache_blk) on the wave it falls to.  At about 200 registers two waves
     // share each SIMD (a second register set per wave measured slower: one wave
     // per SIMD).
-    {
+    if constexpr (kTok) {
+        if (kCols * wave < n_cols) {  // wave-uniform: this wave owns some columns
+            KV16 x;
+            if (n_cache_blk > 0) {
+                load_k(0, x);
+                load_v(0, x);
+            }
+            for (int j = 0; j < n_cache_blk; ++j)
+                compute(j, j + 1, x);
+            if (nblk > n_cache_blk) {
+                load_new(x);
+                compute(n_cache_blk, nblk, x);
+            }
+        }
+    } else {
         KV16 x;
         if (wave < n_cache_blk) {
             load_k(wave, x);
@@ -279,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
 
     // merge: waves 1..3 park (acc, m, l) in LDS; wave 0 folds them in and writes.
     // acc[db][i] holds dim 8*(4kg + i) + db of column lr.
-    if (wave > 0 && col_ok) {
+    if (!kTok && wave > 0 && col_ok) {
         float *e = &merge[wave - 1][lr][0];
         if (kg == 0) {
             e[kDv] = m;
@@ -292,16 +316,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             *(float4 *)&e[d0 + 4] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
         }
     }
-    __syncthreads();
-    if (wave == 0 && col_ok) {
+    if constexpr (!kTok)
+        __syncthreads();
+    if ((kTok || wave == 0) && col_ok) {
         const bool write_final = a.n_splits == 1;
         const size_t rows_total = (size_t)a.B * nq * Hq;
-        const int t = lr / group;
-        const int h = g * group + lr % group;
+        const int t = col / group;
+        const int h = g * group + col % group;
         const size_t row = ((size_t)b * nq + t) * Hq + h;
         float mx = m;
 #pragma unroll
-        for (int w = 0; w < kWaves - 1; ++w)
+        for (int w = 0; w < kMerge; ++w)
             mx = fmaxf(mx, merge[w][lr][kDv]);
         float M = mx, zs = 0.f;
         if (write_final) {
@@ -310,10 +335,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             zs = (sink2 == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(sink2 - M);
         }
         const float f0 = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-        float fw[kWaves - 1];
+        float fw[kMerge > 0 ? kMerge : 1];
         float z = zs + lt * f0;
 #pragma unroll
-        for (int w = 0; w < kWaves - 1; ++w) {
+        for (int w = 0; w < kMerge; ++w) {
             const float mw = merge[w][lr][kDv];
             fw[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
             z += merge[w][lr][kDv + 1] * fw[w];
@@ -327,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             for (int db = 0; db < 8; ++db)
                 vals[db] = acc[db][i] * f0;
 #pragma unroll
-            for (int w = 0; w < kWaves - 1; ++w) {
+            for (int w = 0; w < kMerge; ++w) {
                 const float4 p0 = *(const float4 *)&merge[w][lr][d0];
                 const float4 p1 = *(const float4 *)&merge[w][lr][d0 + 4];
                 vals[0] += p0.x * fw[w];
@@ -365,7 +390,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
 hipError_t launch_decode16(const CachedArgs &a, hipStream_t s) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 grid((unsigned)(a.B * a.Hkv * a.n_splits)), block(kThreads);
-    decode16_kernel<<<grid, block, 0, s>>>(a, scale_log2);
+    if (a.nq * (a.Hq / a.Hkv) <= kCols)
+        decode16_kernel<false><<<grid, block, 0, s>>>(a, scale_log2);
+    else
+        decode16_kernel<true><<<grid, block, 0, s>>>(a, scale_log2);
     return hipGetLastError();
 }
 

@@ -70,6 +70,8 @@ hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s);
 hipError_t launch_decode16(const CachedArgs &a, hipStream_t s);
 hipError_t launch_cached_f32(const CachedArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int bf16, hipStream_t s);
+hipError_t launch_advance_len(int32_t *cache_len, const int32_t *n_accept, int B, int n,
+                              hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -60,6 +60,7 @@ def _bind(lib):
         "sinkattn_verify": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32, i32,
                              i32, f32, i32, p, sz, i32, p], i32),
         "sinkattn_kv_append": ([p, p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, i32, p], i32),
+        "sinkattn_advance_len": ([p, p, i32, i32, p], i32),
         "sinkattn_prefill_global_rope": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32,
                                           i32, f64, i32, p], i32),
         "sinkattn_decode_rope": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32,
@@ -91,7 +92,8 @@ def lib():
 EXPORTED = ["sinkattn_abi_version", "sinkattn_status_string", "sinkattn_rope_partial",
             "sinkattn_prefill_swa", "sinkattn_prefill_swa_rope", "sinkattn_prefill_global", "sinkattn_decode_workspace_bytes",
             "sinkattn_decode", "sinkattn_verify", "sinkattn_kv_append",
-            "sinkattn_prefill_global_rope", "sinkattn_decode_rope", "sinkattn_verify_rope"]
+            "sinkattn_prefill_global_rope", "sinkattn_decode_rope", "sinkattn_verify_rope",
+            "sinkattn_advance_len"]
 
 
 def _check(rc: int):
@@ -320,6 +322,16 @@ def kv_append(k_new, v_new, k_cache, v_cache, cache_len, kind=RING, n_accept=Non
     _check(lib().sinkattn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                     int(kind), cap, _ptr(cache_len), _ptr(n_accept), B, n, Hkv,
                                     dqk, dv, _dtype_code(k_new), _stream()))
+
+
+def advance_len(cache_len, n, n_accept=None):
+    """cache_len[b] += min(n_accept[b], n) (n when n_accept is None), on the device."""
+    _dev(cache_len, n_accept)
+    if cache_len.dtype != torch.int32 or (n_accept is not None and n_accept.dtype != torch.int32):
+        raise SinkAttnError(-3, "cache_len and n_accept are int32")
+    _check(lib().sinkattn_advance_len(_ptr(cache_len), _ptr(n_accept), cache_len.numel(), int(n),
+                                      _stream()))
+    return cache_len
 
 
 def default_scale(dqk: int = DQK) -> float:

@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(ops.EXPORTED) == names
@@ -161,6 +161,15 @@ def test_decode_verify_rope_validation(lib):
     assert ver(nq=9) == SHAPE
     assert ver(k_rot=P(FAKE[1].value + 32)) == ALIAS   # k_rot over k_new
     assert ver(k_rot=P(FAKE[9].value + 32)) == ALIAS   # k_rot over o
+
+
+def test_advance_len_validation(lib):
+    f = lib.sinkattn_advance_len
+    assert f(None, None, 4, 4, None) == NULL
+    assert f(FAKE[0], None, -1, 4, None) == SHAPE
+    assert f(FAKE[0], FAKE[1], 4, -1, None) == SHAPE
+    assert f(FAKE[0], P(FAKE[0].value + 4), 4, 4, None) == ALIAS
+    assert f(FAKE[0], FAKE[1], 0, 4, None) == OK   # nothing to do, no HIP call
 
 
 def test_rope_and_append_validation(lib):
