@@ -204,3 +204,64 @@ def decode_or_verify(q, k_hist, v_hist, k_new, v_new, cache_len, sink, window: i
         outs.append(o)
         lses.append(lse)
     return np.stack(outs), np.stack(lses)
+
+
+# ---------------------------------------------------------------------------
+# FP8 KV cache.  The report runs inference in FP8 but does not give the format
+# or the scaling of the attention cache.  Reading taken here: the OCP 8-bit
+# floating point E4M3 format (sign, 4 exponent bits with bias 7, 3 mantissa
+# bits; no infinities; S.1111.111 is NaN; largest finite value 448), one scale
+# per tensor (cache value = code value * scale), and a quantizer that divides in
+# IEEE fp32 and rounds that quotient once to the nearest E4M3 value, ties to the
+# even code, saturating beyond +-448.
+# ---------------------------------------------------------------------------
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 code, from the format's definition (fp64, exact)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+# the finite non-negative values, codes 0x00 .. 0x7E in increasing order
+_E4M3_TABLE = fp8_e4m3_decode(np.arange(0x7F))
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """Nearest finite E4M3 code to each value (a search over the value table):
+    ties go to the even code, magnitudes beyond 448 saturate to +-448, the sign
+    of zero is kept.  NaN inputs are rejected."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any():
+        raise ValueError("fp8_e4m3_encode: NaN input")
+    a = np.abs(x).ravel()
+    hi = np.clip(np.searchsorted(_E4M3_TABLE, a, side="left"), 0, len(_E4M3_TABLE) - 1)
+    lo = np.clip(hi - 1, 0, None)
+    d_hi = np.abs(_E4M3_TABLE[hi] - a)
+    d_lo = np.abs(a - _E4M3_TABLE[lo])
+    pick = np.where(d_lo < d_hi, lo, hi)
+    tie = d_lo == d_hi
+    pick = np.where(tie, np.where(lo % 2 == 0, lo, hi), pick)
+    pick = np.where(a >= _E4M3_TABLE[-1], len(_E4M3_TABLE) - 1, pick)
+    codes = pick.astype(np.uint8) | np.where(np.signbit(x.ravel()), 0x80, 0).astype(np.uint8)
+    return codes.reshape(x.shape)
+
+
+def fp8_quantize(x, scale: float) -> np.ndarray:
+    """Cache codes of values x (each exactly representable in fp32, e.g. bf16)
+    under a per-tensor scale: E4M3(fl32(x / scale))."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().float().numpy()
+    q = np.asarray(x, dtype=np.float32) / np.float32(scale)
+    return fp8_e4m3_encode(q.astype(np.float64))
+
+
+def fp8_dequantize(codes, scale: float) -> np.ndarray:
+    """Cache values: code value * scale (fp64; exact for an fp32 scale)."""
+    if hasattr(codes, "detach"):
+        codes = codes.detach().cpu().numpy()
+    return fp8_e4m3_decode(np.asarray(codes).view(np.uint8)) * float(np.float32(scale))
