@@ -249,35 +249,57 @@ def _graph_time(torch, fn, reps=20):
     return t.mean_ms(), g
 
 
-def run_hybrid_decode(torch, ops, synth, dev):
+FP8_K_SCALE, FP8_V_SCALE = 0.011, 0.0073  # per-tensor E4M3 scales for N(0,1) K / V
+
+
+def run_hybrid_decode(torch, ops, synth, dev, fp8=False):
+    """One decode step of the hybrid block (5 SWA ring layers + 1 global layer) at
+    batch 32 over contexts drawn from [16K, 128K]; bf16 caches, or E4M3 caches
+    (fp8=True) filled by kv_append_fp8 from the same kind of N(0,1) rows."""
     w = synth.WORKLOADS[4]
     B, Hq = w.B, 64
     g = synth.generator(w.seed)
     cl = synth.cache_lengths(g, B, 16384, 131072)
     cap = 131072 + 8
+    cdt = torch.uint8 if fp8 else torch.bfloat16
+    zeros1 = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def fill(kc, vc, seed, n_tok):
+        """Rows of N(0,1) keys / values at positions 0..n_tok-1 of a [1,Hkv,cap,d] cache."""
+        Hkv = kc.shape[1]
+        if not fp8:
+            synth.device_normal(seed, None, device=dev, out=kc[0, :, :n_tok])
+            synth.device_normal(seed + 1, None, device=dev, out=vc[0, :, :n_tok])
+            return
+        k = synth.device_normal(seed, (1, n_tok, Hkv, 192), device=dev)
+        v = synth.device_normal(seed + 1, (1, n_tok, Hkv, 128), device=dev)
+        ops.kv_append_fp8(k, v, kc, vc, zeros1, ops.CONTIG if n_tok > 128 else ops.RING,
+                          k_scale=FP8_K_SCALE, v_scale=FP8_V_SCALE)
+        del k, v
+
     rings = []
     for layer in range(5):
         s0 = w.seed * 100 + layer * 10
-        rings.append(dict(
-            q=synth.device_normal(s0, (B, Hq, 192), device=dev),
-            kn=synth.device_normal(s0 + 1, (B, 8, 192), device=dev),
-            vn=synth.device_normal(s0 + 2, (B, 8, 128), device=dev),
-            kc=synth.device_normal(s0 + 3, (B, 8, 128, 192), device=dev),
-            vc=synth.device_normal(s0 + 4, (B, 8, 128, 128), device=dev),
-            sink=synth.device_normal(s0 + 5, (Hq,), torch.float32, device=dev),
-            o=torch.empty(B, Hq, 128, dtype=torch.bfloat16, device=dev)))
+        r = dict(q=synth.device_normal(s0, (B, Hq, 192), device=dev),
+                 kn=synth.device_normal(s0 + 1, (B, 8, 192), device=dev),
+                 vn=synth.device_normal(s0 + 2, (B, 8, 128), device=dev),
+                 kc=torch.empty(B, 8, 128, 192, dtype=cdt, device=dev),
+                 vc=torch.empty(B, 8, 128, 128, dtype=cdt, device=dev),
+                 sink=synth.device_normal(s0 + 5, (Hq,), torch.float32, device=dev),
+                 o=torch.empty(B, Hq, 128, dtype=torch.bfloat16, device=dev))
+        for b in range(B):
+            fill(r["kc"][b:b + 1], r["vc"][b:b + 1], s0 + 3000 + 2 * b, 128)
+        rings.append(r)
     s0 = w.seed * 100 + 90
     gl = dict(q=synth.device_normal(s0, (B, Hq, 192), device=dev),
               kn=synth.device_normal(s0 + 1, (B, 4, 192), device=dev),
               vn=synth.device_normal(s0 + 2, (B, 4, 128), device=dev),
-              kc=torch.empty(B, 4, cap, 192, dtype=torch.bfloat16, device=dev),
-              vc=torch.empty(B, 4, cap, 128, dtype=torch.bfloat16, device=dev),
+              kc=torch.empty(B, 4, cap, 192, dtype=cdt, device=dev),
+              vc=torch.empty(B, 4, cap, 128, dtype=cdt, device=dev),
               sink=synth.device_normal(s0 + 5, (Hq,), torch.float32, device=dev),
               o=torch.empty(B, Hq, 128, dtype=torch.bfloat16, device=dev))
     for b in range(B):
-        L = int(cl[b])
-        synth.device_normal(s0 + 1000 + b, None, device=dev, out=gl["kc"][b, :, :L])
-        synth.device_normal(s0 + 2000 + b, None, device=dev, out=gl["vc"][b, :, :L])
+        fill(gl["kc"][b:b + 1], gl["vc"][b:b + 1], s0 + 1000 + 2 * b, int(cl[b]))
     cl_d = cl.to(dev)
     max_len = int(cl.max())
     ws = torch.empty(ops.decode_workspace_bytes(B, Hq, 1, 256) // 4, dtype=torch.float32,
@@ -285,13 +307,23 @@ def run_hybrid_decode(torch, ops, synth, dev):
 
     # each layer: RoPE of the new token fused, attention, new token stored in the cache
     def swa(r):
-        ops.decode_rope(r["q"], r["kn"], r["vn"], r["kc"], r["vc"], cl_d, r["sink"], ops.RING,
-                        128, max_len, base=synth.BASE_SWA, out=r["o"])
+        if fp8:
+            ops.decode_fp8(r["q"], r["kn"], r["vn"], r["kc"], r["vc"], cl_d, r["sink"], ops.RING,
+                           128, max_len, FP8_K_SCALE, FP8_V_SCALE, rope=(synth.BASE_SWA, 64),
+                           out=r["o"])
+        else:
+            ops.decode_rope(r["q"], r["kn"], r["vn"], r["kc"], r["vc"], cl_d, r["sink"],
+                            ops.RING, 128, max_len, base=synth.BASE_SWA, out=r["o"])
 
     def glob():
-        ops.decode_rope(gl["q"], gl["kn"], gl["vn"], gl["kc"], gl["vc"], cl_d, gl["sink"],
-                        ops.CONTIG, 0, max_len, base=synth.BASE_GA, num_splits=0, workspace=ws,
-                        out=gl["o"])
+        if fp8:
+            ops.decode_fp8(gl["q"], gl["kn"], gl["vn"], gl["kc"], gl["vc"], cl_d, gl["sink"],
+                           ops.CONTIG, 0, max_len, FP8_K_SCALE, FP8_V_SCALE,
+                           rope=(synth.BASE_GA, 64), num_splits=0, workspace=ws, out=gl["o"])
+        else:
+            ops.decode_rope(gl["q"], gl["kn"], gl["vn"], gl["kc"], gl["vc"], cl_d, gl["sink"],
+                            ops.CONTIG, 0, max_len, base=synth.BASE_GA, num_splits=0,
+                            workspace=ws, out=gl["o"])
 
     def block():
         for r in rings:
@@ -312,14 +344,16 @@ def run_hybrid_decode(torch, ops, synth, dev):
     swa_ms, glob_ms = ts.mean_ms(), tg.mean_ms()
     keys_g = int((cl.to(torch.int64) + 1).sum()) * 4
     keys_s = B * 8 * 128
-    kv_g = keys_g * 640
-    kv_s = keys_s * 640
+    per_key = 320 if fp8 else 640  # K + V bytes per key and KV head
+    kv_g = keys_g * per_key
+    kv_s = keys_s * per_key
     qo = B * Hq * (192 + 128) * 2
     total_kv = 5 * kv_s + kv_g
     total_bytes = total_kv + 6 * qo
     gflops = 2 * keys_g * 16 * 320  # 16 query heads per KV head, 640 FLOP per pair
     del gl, rings
-    return dict(workload=w.name, step_ms=step_ms, kv_bytes=total_kv, bytes=total_bytes,
+    return dict(workload=w.name + ("_e4m3kv" if fp8 else ""), step_ms=step_ms,
+                kv_bytes=total_kv, bytes=total_bytes,
                 kv_gbs=total_kv / step_ms / 1e6, hbm_frac=total_bytes / step_ms / 1e6 / PEAK_HBM_GBS,
                 swa_layer_ms=swa_ms, swa_layer_gbs=(kv_s + qo) / swa_ms / 1e6,
                 global_ms=glob_ms, global_gbs=(kv_g + qo) / glob_ms / 1e6,
@@ -627,6 +661,10 @@ def main():
         if "decode" in only:
             log("[bench] hybrid-block decode B=32")
             others["hybrid_decode"] = run_hybrid_decode(torch, ops, synth, dev)
+            log("[bench] hybrid-block decode B=32, E4M3 KV caches")
+            others["hybrid_decode_fp8"] = run_hybrid_decode(torch, ops, synth, dev, fp8=True)
+            others["hybrid_decode_fp8"]["speedup_vs_bf16"] = (
+                others["hybrid_decode"]["step_ms"] / others["hybrid_decode_fp8"]["step_ms"])
         if "spec" in only:
             log("[bench] self-speculative step B=64 ctx 16384")
             others["spec_loop"] = run_spec_loop(torch, ops, synth, dev)

@@ -234,6 +234,44 @@ int sinkattn_kv_append(const void *k_new, const void *v_new, void *k_cache, void
                        int B, int n, int Hkv, int dqk, int dv, int dtype, void *stream);
 
 /*
+ * FP8 KV caches.  The report runs training and inference in FP8 (Section 4.6)
+ * without defining the attention cache format; these entry points keep the
+ * caches as OCP E4M3 codes (1 byte per element: sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; no infinities; largest finite 448) with one scale
+ * per tensor: cached value = code value * k_scale (keys) or * v_scale (values).
+ * Activations (q, k_new, v_new, o, k_rot) are bf16.  A value x is stored as
+ * the nearest E4M3 value of fl32(x / scale), ties to the even code, saturating
+ * at +-448 (never NaN).  The new tokens of a step attend at bf16 precision
+ * (read from k_new / v_new, as in sinkattn_decode) and are stored quantized.
+ *   sinkattn_decode_fp8 / sinkattn_verify_fp8: as sinkattn_decode /
+ *     sinkattn_verify (k_cache, v_cache: [B,Hkv,cap,192] / [B,Hkv,cap,128]
+ *     uint8 codes); rope_dim = 0 takes q and k_new as already rotated,
+ *     rope_dim = 64 fuses the RoPE as sinkattn_decode_rope / verify_rope do
+ *     (k_rot, verify only, requires rope_dim = 64: bf16 rotated keys out).
+ *   sinkattn_kv_append_fp8: as sinkattn_kv_append, quantizing bf16 rows.
+ * Errors: k_scale or v_scale not finite and > 0 -> SINKATTN_ERR_SHAPE; other
+ * codes as for the bf16 entry points.
+ */
+int sinkattn_decode_fp8(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                        void *v_cache, int kind, int cap, const int32_t *cache_len,
+                        int max_len_hint, const float *sink, void *o, int B, int Hq, int Hkv,
+                        int dqk, int dv, int window, float scale, float k_scale, float v_scale,
+                        int rope_dim, double rope_base, int num_splits, void *workspace,
+                        size_t ws_bytes, void *stream);
+
+int sinkattn_verify_fp8(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                        const void *v_cache, int kind, int cap, const int32_t *cache_len,
+                        int max_len_hint, const float *sink, void *o, void *k_rot, int B,
+                        int nq, int Hq, int Hkv, int dqk, int dv, int window, float scale,
+                        float k_scale, float v_scale, int rope_dim, double rope_base,
+                        int num_splits, void *workspace, size_t ws_bytes, void *stream);
+
+int sinkattn_kv_append_fp8(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                           int kind, int cap, const int32_t *cache_len, const int32_t *n_accept,
+                           int B, int n, int Hkv, int dqk, int dv, float k_scale, float v_scale,
+                           void *stream);
+
+/*
  * Advance the cached lengths after a commit (Section 2.3.1: accepted draft
  * tokens join the context): cache_len[b] += min(max(n_accept[b], 0), n), or
  * += n when n_accept is NULL -- exactly the tokens sinkattn_kv_append stored

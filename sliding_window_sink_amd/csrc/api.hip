@@ -108,10 +108,18 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
                   const float *sink, void *o, int B, int nq, int Hq, int Hkv, int dqk, int dv,
                   int window, float scale, int num_splits, void *workspace, size_t ws_bytes,
                   int dtype, void *stream, int write_new, int rope = 0, int rope_dim = 0,
-                  double rope_base = 0.0, void *k_rot = nullptr) {
+                  double rope_base = 0.0, void *k_rot = nullptr, int fp8 = 0,
+                  float k_scale = 1.f, float v_scale = 1.f) {
     int st = check_heads(Hq, Hkv, dqk, dv, dtype);
     if (st)
         return st;
+    if (fp8) {
+        if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) ||
+            !std::isfinite(v_scale))
+            return SINKATTN_ERR_SHAPE;
+        if (dtype != SINKATTN_BF16)
+            return SINKATTN_ERR_UNSUPPORTED;
+    }
     if (rope) {
         if (!(rope_base > 0.0) || !std::isfinite(rope_base) || rope_dim < 0 ||
             rope_dim % 2 != 0 || rope_dim > dqk)
@@ -142,7 +150,8 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
     }
     const size_t es = esize(dtype);
     const size_t on = (size_t)B * nq * Hq * kDv * es;
-    const size_t kcn = (size_t)B * Hkv * cap * kDqk * es, vcn = (size_t)B * Hkv * cap * kDv * es;
+    const size_t ces = fp8 ? 1 : es;  // bytes per cached element
+    const size_t kcn = (size_t)B * Hkv * cap * kDqk * ces, vcn = (size_t)B * Hkv * cap * kDv * ces;
     const size_t qn = (size_t)B * nq * Hq * kDqk * es;
     const size_t knn = (size_t)B * nq * Hkv * kDqk * es, vnn = (size_t)B * nq * Hkv * kDv * es;
     if (k_rot && (overlaps(k_rot, knn, q, qn) || overlaps(k_rot, knn, k_new, knn) ||
@@ -222,6 +231,9 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
     a.rope = rope;
     a.rope_base = rope_base;
     a.k_rot = k_rot;
+    a.fp8 = fp8;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     hipStream_t s = (hipStream_t)stream;
     return status_from_hip(dtype == SINKATTN_BF16 ? launch_cached_bf16(a, s)
                                                   : launch_cached_f32(a, s));
@@ -439,6 +451,63 @@ int sinkattn_kv_append(const void *k_new, const void *v_new, void *k_cache, void
     AppendArgs a{k_new, v_new, k_cache, v_cache, cache_len, n_accept, B, n, Hkv, cap,
                  kind == SINKATTN_CACHE_RING};
     return status_from_hip(launch_append(a, dtype == SINKATTN_BF16, (hipStream_t)stream));
+}
+
+int sinkattn_decode_fp8(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                        void *v_cache, int kind, int cap, const int32_t *cache_len,
+                        int max_len_hint, const float *sink, void *o, int B, int Hq, int Hkv,
+                        int dqk, int dv, int window, float scale, float k_scale, float v_scale,
+                        int rope_dim, double rope_base, int num_splits, void *workspace,
+                        size_t ws_bytes, void *stream) {
+    return cached_common(q, k_new, v_new, k_cache, v_cache, kind, cap, cache_len, max_len_hint,
+                         sink, o, B, 1, Hq, Hkv, dqk, dv, window, scale, num_splits, workspace,
+                         ws_bytes, SINKATTN_BF16, stream, 1, rope_dim != 0, rope_dim, rope_base,
+                         nullptr, 1, k_scale, v_scale);
+}
+
+int sinkattn_verify_fp8(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                        const void *v_cache, int kind, int cap, const int32_t *cache_len,
+                        int max_len_hint, const float *sink, void *o, void *k_rot, int B,
+                        int nq, int Hq, int Hkv, int dqk, int dv, int window, float scale,
+                        float k_scale, float v_scale, int rope_dim, double rope_base,
+                        int num_splits, void *workspace, size_t ws_bytes, void *stream) {
+    if (k_rot && rope_dim == 0)
+        return SINKATTN_ERR_SHAPE;  // rotated keys exist only with the RoPE fused
+    return cached_common(q, k_new, v_new, (void *)k_cache, (void *)v_cache, kind, cap,
+                         cache_len, max_len_hint, sink, o, B, nq, Hq, Hkv, dqk, dv, window,
+                         scale, num_splits, workspace, ws_bytes, SINKATTN_BF16, stream, 0,
+                         rope_dim != 0, rope_dim, rope_base, k_rot, 1, k_scale, v_scale);
+}
+
+int sinkattn_kv_append_fp8(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                           int kind, int cap, const int32_t *cache_len, const int32_t *n_accept,
+                           int B, int n, int Hkv, int dqk, int dv, float k_scale, float v_scale,
+                           void *stream) {
+    if (kind != SINKATTN_CACHE_RING && kind != SINKATTN_CACHE_CONTIG)
+        return SINKATTN_ERR_UNSUPPORTED;
+    if (!k_new || !v_new || !k_cache || !v_cache || !cache_len)
+        return SINKATTN_ERR_NULL_PTR;
+    if (B < 0 || n < 0 || Hkv <= 0 || cap < 1 || dqk <= 0 || dv <= 0 || !(k_scale > 0.f) ||
+        !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+        return SINKATTN_ERR_SHAPE;
+    if (dqk != kDqk || dv != kDv)
+        return SINKATTN_ERR_UNSUPPORTED;
+    if ((int64_t)B * n * Hkv > INT_MAX / 64)
+        return SINKATTN_ERR_SHAPE;
+    const size_t kcn = (size_t)B * Hkv * cap * kDqk, vcn = (size_t)B * Hkv * cap * kDv;
+    const size_t knn = (size_t)B * n * Hkv * kDqk * 2, vnn = (size_t)B * n * Hkv * kDv * 2;
+    if (overlaps(k_cache, kcn, v_cache, vcn) || overlaps(k_cache, kcn, k_new, knn) ||
+        overlaps(k_cache, kcn, v_new, vnn) || overlaps(v_cache, vcn, k_new, knn) ||
+        overlaps(v_cache, vcn, v_new, vnn))
+        return SINKATTN_ERR_ALIAS;
+    if (B == 0 || n == 0)
+        return SINKATTN_OK;
+    AppendArgs a{k_new, v_new, k_cache, v_cache, cache_len, n_accept, B, n, Hkv, cap,
+                 kind == SINKATTN_CACHE_RING};
+    a.fp8 = 1;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    return status_from_hip(launch_append(a, 1, (hipStream_t)stream));
 }
 
 int sinkattn_advance_len(int32_t *cache_len, const int32_t *n_accept, int B, int n,

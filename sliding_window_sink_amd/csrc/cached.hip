@@ -482,15 +482,16 @@ __global__ void append_kernel(AppendArgs a, int row_bytes_k, int row_bytes_v) {
     }
     const size_t crow = ((size_t)b * a.Hkv + g) * a.cap + slot;
     const size_t nrow = ((size_t)b * a.n + t) * a.Hkv + g;
-    if (piece < pk) {
-        const char *src = (const char *)a.k_new + nrow * row_bytes_k + piece * 16;
-        char *dst = (char *)a.k_cache + crow * row_bytes_k + piece * 16;
-        *(uint4 *)dst = *(const uint4 *)src;
+    const bool is_k = piece < pk;
+    const int pc = is_k ? piece : piece - pk;
+    const int rb = is_k ? row_bytes_k : row_bytes_v;
+    const uint4 x = *(const uint4 *)((const char *)(is_k ? a.k_new : a.v_new) + nrow * rb + pc * 16);
+    if (a.fp8) {  // 8 bf16 -> 8 E4M3 codes of x / scale; cache rows are 1 byte per dim
+        char *dst = (char *)(is_k ? a.k_cache : a.v_cache) + crow * (rb / 2) + pc * 8;
+        *(uint2 *)dst = bf16x8_to_e4m3x8(x, is_k ? a.k_scale : a.v_scale);
     } else {
-        const int pc = piece - pk;
-        const char *src = (const char *)a.v_new + nrow * row_bytes_v + pc * 16;
-        char *dst = (char *)a.v_cache + crow * row_bytes_v + pc * 16;
-        *(uint4 *)dst = *(const uint4 *)src;
+        char *dst = (char *)(is_k ? a.k_cache : a.v_cache) + crow * rb + pc * 16;
+        *(uint4 *)dst = x;
     }
 }
 
@@ -501,10 +502,10 @@ hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 grid((unsigned)(a.B * a.Hkv * a.n_splits)), block(kThreads);
     // <= 16 columns, or a short window (each workgroup's key range is a few
-    // blocks, so streaming it once per 16-column wave costs little): the
-    // 16-column kernel; long ranges with more columns: the 32-column kernel,
-    // whose waves split the key blocks.
-    if (n_cols <= 16 || (a.window > 0 && a.window <= 4096)) {
+    // blocks, so streaming it once per 16-column wave costs little), or E4M3
+    // caches: the 16-column kernel; long ranges with more columns: the
+    // 32-column kernel, whose waves split the key blocks.
+    if (a.fp8 || n_cols <= 16 || (a.window > 0 && a.window <= 4096)) {
         const hipError_t e16 = launch_decode16(a, s);
         if (e16 != hipSuccess)
             return e16;

@@ -179,29 +179,85 @@ __device__ __forceinline__ uint4 rope_chunk_bf16(uint4 x, const float2 *cs) {
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// ---- FP8 (OCP E4M3) cache codes ----
+// Two E4M3 codes (bytes 0,1, or 2,3 with kHi, of w) to two bf16, exactly (every E4M3 value
+// is a bf16 value; the gfx950 conversion follows the OCP definition, scale 1).
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi);
+    return __builtin_bit_cast(uint32_t, r);
+}
+// 8 codes (one uint2) -> 8 bf16 (one uint4), element order kept.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
+    return make_uint4(e4m3x2_to_bf16x2<false>(c.x), e4m3x2_to_bf16x2<true>(c.x),
+                      e4m3x2_to_bf16x2<false>(c.y), e4m3x2_to_bf16x2<true>(c.y));
+}
+// Nearest E4M3 code of a finite fp32 value, ties to the even code, magnitudes
+// past 448 saturate (never the NaN code).  Integer rounding of the fp32 fields.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+    const uint32_t bits = __builtin_bit_cast(uint32_t, v);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const float a = __builtin_fabsf(v);
+    uint32_t code;
+    if (!(a < 448.0f)) {
+        code = 0x7Eu;
+    } else if (a < 0x1p-6f) {  // E4M3 subnormals: multiples of 2^-9 (8 -> code 0x08)
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        const uint32_t ab = bits & 0x7fffffffu;
+        int e = (int)(ab >> 23) - 127;           // -6 .. 8
+        const uint32_t m = ab & 0x7fffffu;
+        uint32_t q = (m + 0x7ffffu + ((m >> 20) & 1u)) >> 20;  // RNE to 3 bits
+        if (q == 8u) {
+            q = 0u;
+            ++e;
+        }
+        code = ((uint32_t)(e + 7) << 3) | q;
+        code = code > 0x7Eu ? 0x7Eu : code;
+    }
+    return code | sign;
+}
+// 8 bf16 (one uint4) -> 8 codes of (x / scale), the quotient rounded once to fp32.
+__device__ __forceinline__ uint2 bf16x8_to_e4m3x8(uint4 x, float scale) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint16_t h = (uint16_t)((w[i >> 1] >> ((i & 1) * 16)) & 0xffffu);
+        const uint32_t c = f32_to_e4m3(__fdiv_rn(bf16_bits_to_f32(h), scale));
+        out[i >> 2] |= c << ((i & 3) * 8);
+    }
+    return make_uint2(out[0], out[1]);
+}
+
 // New-token side effects of a decode / verify launch, done by one workgroup per
 // (sequence, KV head): decode stores token 0 into the cache at position P (its
 // k rotated when kRope); with kRope a k_rot output receives every new token's
 // rotated k.  tab holds the (cos, sin) of positions P .. P+nq-1 when kRope.  Nothing in
 // the launch reads the rows written here.
-template <bool kRope>
+template <bool kRope, bool kFp8 = false>
 __device__ __forceinline__ void cached_store_new(const CachedArgs &a, size_t crow0, size_t nrow0,
                                                  int P, const float2 *tab, int tid,
                                                  int nthreads) {
     const uint16_t *ks = (const uint16_t *)a.k_new;
     if (a.write_new && (a.ring || P < a.cap)) {
         const int slot = a.ring ? (P % a.cap) : P;
-        uint16_t *kd = (uint16_t *)a.k_cache + (crow0 + slot) * kDqk;
-        uint16_t *vd = (uint16_t *)a.v_cache + (crow0 + slot) * kDv;
         const uint16_t *vs = (const uint16_t *)a.v_new + nrow0 * kDv;
         for (int i = tid; i < (kDqk + kDv) / 8; i += nthreads) {
-            if (i < kDqk / 8) {
-                uint4 x = *(const uint4 *)(ks + nrow0 * kDqk + i * 8);
-                if (kRope && i < 8)
-                    x = rope_chunk_bf16(x, tab + 4 * i);
-                *(uint4 *)(kd + i * 8) = x;
+            const bool is_k = i < kDqk / 8;
+            const int ci = is_k ? i : i - kDqk / 8;
+            uint4 x = is_k ? *(const uint4 *)(ks + nrow0 * kDqk + ci * 8)
+                           : *(const uint4 *)(vs + ci * 8);
+            if (kRope && is_k && ci < 8)
+                x = rope_chunk_bf16(x, tab + 4 * ci);
+            const size_t row = (crow0 + slot) * (is_k ? kDqk : kDv) + ci * 8;
+            if constexpr (kFp8) {
+                uint8_t *dst = (uint8_t *)(is_k ? a.k_cache : a.v_cache) + row;
+                *(uint2 *)dst = bf16x8_to_e4m3x8(x, is_k ? a.k_scale : a.v_scale);
             } else {
-                *(uint4 *)(vd + (i - kDqk / 8) * 8) = *(const uint4 *)(vs + (i - kDqk / 8) * 8);
+                uint16_t *dst = (uint16_t *)(is_k ? a.k_cache : a.v_cache) + row;
+                *(uint4 *)dst = x;
             }
         }
     }

@@ -29,6 +29,8 @@
 // the new token into the cache in the same launch (the attention reads
 // positions >= P from k_new).  Chunks that hold no key return at once: the
 // combine only reads the chunks that intersect the visible range.
+#include <type_traits>
+
 #include "common.h"
 
 namespace sinkattn {
@@ -49,13 +51,44 @@ __device__ __forceinline__ f32x4v mfma16x16x32(const bf16x8 &a, const bf16x8 &b,
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// One block of 32 keys in operand layout.  bf16 rows (the cache, or the new
+// tokens):
 struct KV16 {
-    uint4 k[2][kDqk / 32];  // key tile kt (keys 16kt + l%16), k-step s: dims 32s + 8(l/16) .. +7
+    uint4 k[2][kDqk / 32];  // key tile kt (keys 16kt + l%16), k-step s: dims kdim0(s) .. +7
     uint4 v[8];             // key (e/4)*16 + 4(l/16) + e%4, dims 8(l%16) .. +7
 };
+// E4M3 cache rows: K as 16-byte runs (dims 64u + 16(l/16) .. +15 serve k-steps
+// 2u and 2u+1), V as 8-byte runs (dims 8(l%16) .. +7); converted to bf16 in
+// registers just before the MFMAs.
+struct KV8 {
+    uint4 k[2][kDqk / 64];
+    uint2 v[8];
+};
 
-template <bool kTok>
+// First head dim of k-step s for lane group kg.  Any order of the 192 dims
+// works if q and k use the same one; the E4M3 layout pairs k-steps so that one
+// 16-byte load of a 192-byte row feeds two of them.
+template <bool kFp8>
+__device__ __forceinline__ int kdim0(int s, int kg) {
+    return kFp8 ? 64 * (s >> 1) + 16 * kg + 8 * (s & 1) : 32 * s + 8 * kg;
+}
+
+__device__ __forceinline__ bf16x8 k_operand(const KV16 &x, int kt, int s) {
+    return as_bf16x8(x.k[kt][s]);
+}
+__device__ __forceinline__ bf16x8 k_operand(const KV8 &x, int kt, int s) {
+    const uint4 r = x.k[kt][s >> 1];
+    const uint32_t w0 = (s & 1) ? r.z : r.x, w1 = (s & 1) ? r.w : r.y;
+    return as_bf16x8(make_uint4(e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                                e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)));
+}
+__device__ __forceinline__ uint4 v_rows(const KV16 &x, int e) { return x.v[e]; }
+__device__ __forceinline__ uint4 v_rows(const KV8 &x, int e) { return e4m3x8_to_bf16x8(x.v[e]); }
+
+template <bool kTok, bool kFp8>
 __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, float scale_log2) {
+    using KVc = typename std::conditional<kFp8, KV8, KV16>::type;  // cache block registers
+    constexpr uint32_t kEs = kFp8 ? 1 : 2;  // bytes per cached element
     // kTok = false: <= 16 columns, the waves split the key blocks and merge.
     // kTok = true: <= 64 columns, wave w owns columns 16w .. 16w+15 and reads
     // every key block (the 4 waves stream the same rows: one HBM read, L2 hits).
@@ -94,14 +127,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // The chunk holding position P stores the new token (decode) / rotated keys.
     if (P >= rlo && P < rhi) {
         if (a.rope)
-            cached_store_new<true>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
+            cached_store_new<true, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
         else
-            cached_store_new<false>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
+            cached_store_new<false, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
     }
 
     const uint64_t cache_rows = a.ring ? (uint64_t)a.cap : (uint64_t)P;
-    const BufRsrc kc = make_buf((const uint16_t *)a.k_cache + crow0 * kDqk, cache_rows * kDqk * 2);
-    const BufRsrc vc = make_buf((const uint16_t *)a.v_cache + crow0 * kDv, cache_rows * kDv * 2);
+    const BufRsrc kc = make_buf((const uint8_t *)a.k_cache + crow0 * kDqk * kEs,
+                                cache_rows * kDqk * kEs);
+    const BufRsrc vc = make_buf((const uint8_t *)a.v_cache + crow0 * kDv * kEs,
+                                cache_rows * kDv * kEs);
     const BufRsrc kn = make_buf((const uint16_t *)a.k_new + nrow0 * kDqk,
                                 ((uint64_t)(nq - 1) * Hkv + 1) * kDqk * 2);
     const BufRsrc vn = make_buf((const uint16_t *)a.v_new + nrow0 * kDv,
@@ -116,16 +151,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
         const BufRsrc qb = make_buf((const uint16_t *)a.q + (size_t)b * nq * Hq * kDqk,
                                     (uint64_t)nq * Hq * kDqk * 2);
         const uint32_t off =
-            col_ok ? ((uint32_t)((col / group) * Hq + g * group + col % group) * kDqk + (uint32_t)kg * 8) * 2
-                   : kOob;
+            col_ok ? (uint32_t)((col / group) * Hq + g * group + col % group) * kDqk * 2 : kOob;
         uint4 qr[kDqk / 32];
 #pragma unroll
         for (int s = 0; s < kDqk / 32; ++s)
-            qr[s] = buf_load16(qb, off + (uint32_t)s * 64);
-        if (a.rope && col_ok) {  // dims 32s + 8kg .. +7 (s < 2): pairs 16s + 4kg ..
-            const float2 *cs = rope_tab + (col / group) * 32 + 4 * kg;
-            qr[0] = rope_chunk_bf16(qr[0], cs);
-            qr[1] = rope_chunk_bf16(qr[1], cs + 16);
+            qr[s] = buf_load16(qb, off + (uint32_t)kdim0<kFp8>(s, kg) * 2);
+        if (a.rope && col_ok) {  // k-steps 0, 1 hold dims < 64: 8-dim chunk kdim0/8
+            const float2 *cs = rope_tab + (col / group) * 32;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                qr[s] = rope_chunk_bf16(qr[s], cs + 4 * (kdim0<kFp8>(s, kg) / 8));
         }
 #pragma unroll
         for (int s = 0; s < kDqk / 32; ++s)
@@ -151,40 +186,52 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // after PV, so one register set keeps loads in flight through the compute.
     // Cache blocks and the new-token block use separate functions so that every
     // load names one descriptor.
-    auto load_k = [&](int j, KV16 &x) {
+    auto load_k = [&](int j, KVc &x) {
         const int kb = rlo + j * kKb;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const int p = kb + 16 * kt + lr;
             const int slot = a.ring ? p % a.cap : p;
-            const uint32_t off = p < ce ? (uint32_t)slot * kDqk * 2 + (uint32_t)kg * 16 : kOob;
+            if constexpr (kFp8) {
+                const uint32_t off = p < ce ? (uint32_t)slot * kDqk + (uint32_t)kg * 16 : kOob;
 #pragma unroll
-            for (int s = 0; s < kDqk / 32; ++s)
-                x.k[kt][s] = buf_load16(kc, off + (uint32_t)s * 64);
+                for (int u = 0; u < kDqk / 64; ++u)
+                    x.k[kt][u] = buf_load16(kc, off + (uint32_t)u * 64);
+            } else {
+                const uint32_t off = p < ce ? (uint32_t)slot * kDqk * 2 : kOob;
+#pragma unroll
+                for (int s = 0; s < kDqk / 32; ++s)
+                    x.k[kt][s] = buf_load16(kc, off + (uint32_t)kdim0<false>(s, kg) * 2);
+            }
         }
     };
-    auto load_v = [&](int j, KV16 &x) {
+    auto load_v = [&](int j, KVc &x) {
         const int kb = rlo + j * kKb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int p = kb + (e >> 2) * 16 + 4 * kg + (e & 3);
             const int slot = a.ring ? p % a.cap : p;
-            const uint32_t off = p < ce ? (uint32_t)slot * kDv * 2 + (uint32_t)lr * 16 : kOob;
-            x.v[e] = buf_load16(vc, off);
+            const uint32_t off =
+                p < ce ? ((uint32_t)slot * kDv + (uint32_t)lr * 8) * kEs : kOob;
+            if constexpr (kFp8)
+                x.v[e] = buf_load8(vc, off);
+            else
+                x.v[e] = buf_load16(vc, off);
         }
     };
     auto load_new = [&](KV16 &x) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const int p = new_lo + 16 * kt + lr;
-            const uint32_t off = p < rhi ? (uint32_t)(p - P) * krow + (uint32_t)kg * 16 : kOob;
+            const uint32_t off = p < rhi ? (uint32_t)(p - P) * krow : kOob;
 #pragma unroll
             for (int s = 0; s < kDqk / 32; ++s)
-                x.k[kt][s] = buf_load16(kn, off + (uint32_t)s * 64);
+                x.k[kt][s] = buf_load16(kn, off + (uint32_t)kdim0<kFp8>(s, kg) * 2);
             if (a.rope && p < rhi) {
-                const float2 *cs = rope_tab + (p - P) * 32 + 4 * kg;
-                x.k[kt][0] = rope_chunk_bf16(x.k[kt][0], cs);
-                x.k[kt][1] = rope_chunk_bf16(x.k[kt][1], cs + 16);
+                const float2 *cs = rope_tab + (p - P) * 32;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    x.k[kt][s] = rope_chunk_bf16(x.k[kt][s], cs + 4 * (kdim0<kFp8>(s, kg) / 8));
             }
         }
 #pragma unroll
@@ -194,19 +241,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             x.v[e] = buf_load16(vn, off);
         }
     };
-    auto compute = [&](int j, int jn, KV16 &x) {
+    // x is a cache block (KVc, prefetching the wave's next block jn) or the
+    // new-token block (KV16 read from k_new / v_new, bf16 even with E4M3 caches).
+    auto compute = [&](int j, int jn, auto &x) {
+        constexpr bool kCacheRegs = std::is_same<std::decay_t<decltype(x)>, KVc>::value;
+        constexpr bool kScaled = kFp8 && kCacheRegs;  // E4M3 codes: fold the scales in
         const int kb = block_base(j);
         const int kend = j < n_cache_blk ? ce : rhi;
+        const float sl2 = kScaled ? scale_log2 * a.k_scale : scale_log2;
         f32x4v sc[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             sc[kt] = f32x4v{};
 #pragma unroll
             for (int s = 0; s < kDqk / 32; ++s)
-                sc[kt] = mfma16x16x32(as_bf16x8(x.k[kt][s]), qf[s], sc[kt]);
+                sc[kt] = mfma16x16x32(k_operand(x, kt, s), qf[s], sc[kt]);
         }
-        if (jn < n_cache_blk)
-            load_k(jn, x);
+        if constexpr (kCacheRegs) {
+            if (jn < n_cache_blk)
+                load_k(jn, x);
+        }
         // element e of this lane: key kb + (e/4)*16 + 4*kg + e%4, column lr
         const bool full = j < n_cache_blk && kb + kKb <= ce && (window <= 0 || kb >= P + nq - window);
         float xs[8];
@@ -226,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             bm = fmaxf(bm, xs[e]);
         bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
         bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-        bm *= scale_log2;
+        bm *= sl2;
         const bool up = bm > m + kRescaleSlack || (m == -INFINITY && bm > -INFINITY);
         const float mn = up ? bm : m;
         const float alpha = up ? fast_exp2(m - mn) : 1.f;
@@ -236,9 +290,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
         bf16x8 pb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float pr = fast_exp2(__fmaf_rn(xs[e], scale_log2, -mu));
+            const float pr = fast_exp2(__fmaf_rn(xs[e], sl2, -mu));
             ps += pr;
-            pb[e] = (__bf16)pr;
+            pb[e] = (__bf16)(kScaled ? pr * a.v_scale : pr);  // P^T feeds V codes * v_scale
         }
         l = __fmaf_rn(l, alpha, ps);
         if (__builtin_amdgcn_ballot_w64(up) != 0) {
@@ -246,14 +300,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             for (int db = 0; db < 8; ++db)
                 acc[db] *= alpha;
         }
-        // V^T operand of tile db: element e = V[key(e)][8*lr + db]; x.v[e] holds dims
+        // V^T operand of tile db: element e = V[key(e)][8*lr + db]; vr[e] holds dims
         // 8lr..8lr+7 of key(e), so each operand word pairs one 16-bit half of two loads.
+        uint4 vr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            vr[e] = v_rows(x, e);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             uint32_t w[4];
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
-                const uint4 va0 = x.v[2 * e2], va1 = x.v[2 * e2 + 1];
+                const uint4 va0 = vr[2 * e2], va1 = vr[2 * e2 + 1];
                 const uint32_t wa = (db >> 1) == 0 ? va0.x : (db >> 1) == 1 ? va0.y : (db >> 1) == 2 ? va0.z : va0.w;
                 const uint32_t wb = (db >> 1) == 0 ? va1.x : (db >> 1) == 1 ? va1.y : (db >> 1) == 2 ? va1.z : va1.w;
                 w[e2] = (db & 1) ? __builtin_amdgcn_perm(wb, wa, 0x07060302u)
@@ -261,8 +319,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             }
             acc[db] = mfma16x16x32(as_bf16x8(make_uint4(w[0], w[1], w[2], w[3])), pb, acc[db]);
         }
-        if (jn < n_cache_blk)
-            load_v(jn, x);
+        if constexpr (kCacheRegs) {
+            if (jn < n_cache_blk)
+                load_v(jn, x);
+        }
     };
 
     // Cache blocks j = wave, wave+4, ..., then the new-token block (index
@@ -271,29 +331,35 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // per SIMD).
     if constexpr (kTok) {
         if (kCols * wave < n_cols) {  // wave-uniform: this wave owns some columns
-            KV16 x;
-            if (n_cache_blk > 0) {
-                load_k(0, x);
-                load_v(0, x);
+            {
+                KVc x;
+                if (n_cache_blk > 0) {
+                    load_k(0, x);
+                    load_v(0, x);
+                }
+                for (int j = 0; j < n_cache_blk; ++j)
+                    compute(j, j + 1, x);
             }
-            for (int j = 0; j < n_cache_blk; ++j)
-                compute(j, j + 1, x);
             if (nblk > n_cache_blk) {
-                load_new(x);
-                compute(n_cache_blk, nblk, x);
+                KV16 xn;
+                load_new(xn);
+                compute(n_cache_blk, nblk, xn);
             }
         }
     } else {
-        KV16 x;
-        if (wave < n_cache_blk) {
-            load_k(wave, x);
-            load_v(wave, x);
+        {
+            KVc x;
+            if (wave < n_cache_blk) {
+                load_k(wave, x);
+                load_v(wave, x);
+            }
+            for (int j = wave; j < n_cache_blk; j += kWaves)
+                compute(j, j + kWaves, x);
         }
-        for (int j = wave; j < n_cache_blk; j += kWaves)
-            compute(j, j + kWaves, x);
         if (nblk > n_cache_blk && n_cache_blk % kWaves == wave) {
-            load_new(x);
-            compute(n_cache_blk, nblk, x);
+            KV16 xn;
+            load_new(xn);
+            compute(n_cache_blk, nblk, xn);
         }
     }
 
@@ -390,10 +456,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
 hipError_t launch_decode16(const CachedArgs &a, hipStream_t s) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 grid((unsigned)(a.B * a.Hkv * a.n_splits)), block(kThreads);
-    if (a.nq * (a.Hq / a.Hkv) <= kCols)
-        decode16_kernel<false><<<grid, block, 0, s>>>(a, scale_log2);
-    else
-        decode16_kernel<true><<<grid, block, 0, s>>>(a, scale_log2);
+    const bool tok = a.nq * (a.Hq / a.Hkv) > kCols;
+    if (a.fp8) {
+        if (tok)
+            decode16_kernel<true, true><<<grid, block, 0, s>>>(a, scale_log2);
+        else
+            decode16_kernel<false, true><<<grid, block, 0, s>>>(a, scale_log2);
+    } else {
+        if (tok)
+            decode16_kernel<true, false><<<grid, block, 0, s>>>(a, scale_log2);
+        else
+            decode16_kernel<false, false><<<grid, block, 0, s>>>(a, scale_log2);
+    }
     return hipGetLastError();
 }
 

@@ -36,6 +36,8 @@ struct CachedArgs {
     int rope;                   // rotate q and k_new (64 dims, interleaved) at P + t
     double rope_base;
     void *k_rot;                // [B,nq,Hkv,192]: rotated k_new out, or nullptr
+    int fp8;                    // caches hold E4M3 codes: value = code * k_scale / v_scale
+    float k_scale, v_scale;
 };
 
 struct AppendArgs {
@@ -43,6 +45,8 @@ struct AppendArgs {
     void *k_cache, *v_cache;
     const int32_t *cache_len, *n_accept;
     int B, n, Hkv, cap, ring;
+    int fp8 = 0;                // bf16 rows quantized into E4M3 caches
+    float k_scale = 1.f, v_scale = 1.f;
 };
 
 // Clamp a device-side cached length into the range the host validated.

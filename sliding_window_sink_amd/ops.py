@@ -61,6 +61,12 @@ def _bind(lib):
                              i32, f32, i32, p, sz, i32, p], i32),
         "sinkattn_kv_append": ([p, p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, i32, p], i32),
         "sinkattn_advance_len": ([p, p, i32, i32, p], i32),
+        "sinkattn_decode_fp8": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32,
+                                 i32, f32, f32, f32, i32, f64, i32, p, sz, p], i32),
+        "sinkattn_verify_fp8": ([p, p, p, p, p, i32, i32, p, i32, p, p, p, i32, i32, i32, i32,
+                                 i32, i32, i32, f32, f32, f32, i32, f64, i32, p, sz, p], i32),
+        "sinkattn_kv_append_fp8": ([p, p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, f32, f32,
+                                    p], i32),
         "sinkattn_prefill_global_rope": ([p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32,
                                           i32, f64, i32, p], i32),
         "sinkattn_decode_rope": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32,
@@ -93,7 +99,8 @@ EXPORTED = ["sinkattn_abi_version", "sinkattn_status_string", "sinkattn_rope_par
             "sinkattn_prefill_swa", "sinkattn_prefill_swa_rope", "sinkattn_prefill_global", "sinkattn_decode_workspace_bytes",
             "sinkattn_decode", "sinkattn_verify", "sinkattn_kv_append",
             "sinkattn_prefill_global_rope", "sinkattn_decode_rope", "sinkattn_verify_rope",
-            "sinkattn_advance_len"]
+            "sinkattn_advance_len", "sinkattn_decode_fp8", "sinkattn_verify_fp8",
+            "sinkattn_kv_append_fp8"]
 
 
 def _check(rc: int):
@@ -322,6 +329,84 @@ def kv_append(k_new, v_new, k_cache, v_cache, cache_len, kind=RING, n_accept=Non
     _check(lib().sinkattn_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                     int(kind), cap, _ptr(cache_len), _ptr(n_accept), B, n, Hkv,
                                     dqk, dv, _dtype_code(k_new), _stream()))
+
+
+def _cached_fp8(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window, max_len_hint,
+                k_scale, v_scale, rope, num_splits, workspace, scale, out, verify, k_rot=None):
+    _dev(q, k_new, v_new, k_cache, v_cache, cache_len, sink, workspace, out, k_rot)
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise SinkAttnError(-3, "E4M3 caches are uint8 tensors")
+    if q.dtype != torch.bfloat16 or k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise SinkAttnError(-3, "q, k_new, v_new are bfloat16")
+    if cache_len.dtype != torch.int32:
+        raise SinkAttnError(-3, "cache_len must be int32")
+    if max_len_hint is None:
+        raise SinkAttnError(-2, "max_len_hint (host bound on cache_len) is required")
+    if verify:
+        B, nq, Hq, dqk = q.shape
+    else:
+        B, Hq, dqk = q.shape
+        nq = 1
+    Bc, Hkv, cap, dk = k_cache.shape
+    dv = v_cache.shape[3]
+    if Bc != B or dk != dqk or v_cache.shape[:3] != (B, Hkv, cap) or sink.shape != (Hq,):
+        raise SinkAttnError(-2, "cache / query shapes disagree")
+    want_new = (B, nq, Hkv) if verify else (B, Hkv)
+    if tuple(k_new.shape[:-1]) != want_new or tuple(v_new.shape[:-1]) != want_new:
+        raise SinkAttnError(-2, "k_new/v_new shapes disagree")
+    if k_rot is not None and (k_rot.shape != k_new.shape or k_rot.dtype != k_new.dtype):
+        raise SinkAttnError(-2, "k_rot must match k_new")
+    oshape = (B, nq, Hq, dv) if verify else (B, Hq, dv)
+    o = out if out is not None else torch.empty(oshape, dtype=q.dtype, device=q.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    rope_dim, base = (0, 0.0) if rope is None else (int(rope[1]), float(rope[0]))
+    args = [_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), int(kind), cap,
+            _ptr(cache_len), int(max_len_hint), _ptr(sink), _ptr(o)]
+    if verify:
+        args += [_ptr(k_rot), B, nq]
+    else:
+        args.append(B)
+    args += [Hq, Hkv, dqk, dv, int(window), _scale(scale), float(k_scale), float(v_scale),
+             rope_dim, base, int(num_splits), ws_ptr, ws_bytes, _stream()]
+    fn = lib().sinkattn_verify_fp8 if verify else lib().sinkattn_decode_fp8
+    _check(fn(*args))
+    return o
+
+
+def decode_fp8(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind=RING, window=128,
+               max_len_hint=None, k_scale=1.0, v_scale=1.0, rope=None, num_splits=0,
+               workspace=None, scale=None, out=None):
+    """decode() over E4M3 (uint8) caches with per-tensor scales; rope=(base, 64)
+    fuses the partial RoPE, rope=None takes q / k_new as already rotated."""
+    return _cached_fp8(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window,
+                       max_len_hint, k_scale, v_scale, rope, num_splits, workspace, scale, out,
+                       verify=False)
+
+
+def verify_fp8(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind=RING, window=128,
+               max_len_hint=None, k_scale=1.0, v_scale=1.0, rope=None, k_rot=None,
+               num_splits=0, workspace=None, scale=None, out=None):
+    """verify() over E4M3 (uint8) caches; the caches are read-only."""
+    return _cached_fp8(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window,
+                       max_len_hint, k_scale, v_scale, rope, num_splits, workspace, scale, out,
+                       verify=True, k_rot=k_rot)
+
+
+def kv_append_fp8(k_new, v_new, k_cache, v_cache, cache_len, kind=RING, n_accept=None,
+                  k_scale=1.0, v_scale=1.0):
+    """kv_append() into E4M3 (uint8) caches: bf16 rows quantized with the scales."""
+    _dev(k_new, v_new, k_cache, v_cache, cache_len, n_accept)
+    B, n, Hkv, dqk = k_new.shape
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise SinkAttnError(-3, "E4M3 caches are uint8 tensors")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise SinkAttnError(-3, "k_new, v_new are bfloat16")
+    _check(lib().sinkattn_kv_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                        int(kind), k_cache.shape[2], _ptr(cache_len),
+                                        _ptr(n_accept), B, n, Hkv, dqk, v_new.shape[3],
+                                        float(k_scale), float(v_scale), _stream()))
 
 
 def advance_len(cache_len, n, n_accept=None):

@@ -25,12 +25,12 @@ def lib():
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(sinkattn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sinkattn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(ops.EXPORTED) == names
@@ -170,6 +170,32 @@ def test_advance_len_validation(lib):
     assert f(FAKE[0], FAKE[1], 4, -1, None) == SHAPE
     assert f(FAKE[0], P(FAKE[0].value + 4), 4, 4, None) == ALIAS
     assert f(FAKE[0], FAKE[1], 0, 4, None) == OK   # nothing to do, no HIP call
+
+
+def test_fp8_validation(lib):
+    def dec(k_scale=0.5, v_scale=0.5, rope_dim=0, B=2, Hq=16):
+        return lib.sinkattn_decode_fp8(FAKE[0], FAKE[1], FAKE[2], FAKE[3], P(13 << 36), 0, 128,
+                                       FAKE[5], 1000, FAKE[6], FAKE[9], B, Hq, 2, 192, 128, 128,
+                                       0.0, k_scale, v_scale, rope_dim, 1e4, 0, None, 0, None)
+    assert dec(k_scale=0.0) == SHAPE
+    assert dec(v_scale=float("nan")) == SHAPE
+    assert dec(rope_dim=32) == UNSUP
+    assert dec(Hq=15) == SHAPE
+    assert dec(B=0) == OK
+
+    def ver(k_rot=None, rope_dim=64):
+        return lib.sinkattn_verify_fp8(FAKE[0], FAKE[1], FAKE[2], FAKE[3], P(13 << 36), 0, 128,
+                                       FAKE[5], 1000, FAKE[6], FAKE[9], k_rot, 2, 4, 16, 2, 192,
+                                       128, 128, 0.0, 1.0, 1.0, rope_dim, 1e4, 0, None, 0, None)
+    assert ver(k_rot=FAKE[7], rope_dim=0) == SHAPE     # rotated keys need the fused RoPE
+    assert ver(k_rot=P(FAKE[1].value + 32)) == ALIAS
+    a = lib.sinkattn_kv_append_fp8
+    assert a(FAKE[0], FAKE[1], FAKE[2], FAKE[3], 0, 128, None, None, 2, 4, 8, 192, 128, 1.0, 1.0,
+             None) == NULL
+    assert a(FAKE[0], FAKE[1], FAKE[2], FAKE[3], 0, 128, FAKE[4], None, 2, 4, 8, 192, 128, -1.0,
+             1.0, None) == SHAPE
+    assert a(FAKE[0], FAKE[1], FAKE[2], FAKE[3], 0, 128, FAKE[4], None, 0, 4, 8, 192, 128, 1.0,
+             1.0, None) == OK
 
 
 def test_rope_and_append_validation(lib):
