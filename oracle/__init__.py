@@ -53,6 +53,9 @@ def _bind(lib):
     lib.oracle_rope_partial.restype = i32
     lib.oracle_round_bf16.argtypes = [p, p, i64]
     lib.oracle_round_bf16.restype = None
+    lib.oracle_sink_attention_bwd.argtypes = [p, p, p, p, p, p, p, i64, i64, i32, i32, i32,
+                                              i32, i64, d, p, p, p, p]
+    lib.oracle_sink_attention_bwd.restype = i32
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     return lib
@@ -117,6 +120,27 @@ def sink_attention(q, k, v, qpos, kpos, sink, window: int = 0, scale: float | No
     if rc != 0:
         raise ValueError("oracle_sink_attention failed (%d)" % rc)
     return o, lse
+
+
+def sink_attention_bwd(q, k, v, qpos, kpos, sink, dout, window: int = 0,
+                       scale: float | None = None, lib=None):
+    """Gradients (dq, dk, dv, dsink) of sink_attention for the upstream gradient
+    dout of o; same layouts as sink_attention (Section 2.2, chain rule)."""
+    lib = lib or load_library()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    qpos, kpos, sink = _i64(qpos), _i64(kpos), _f64(sink)
+    nq, hq, dqk = q.shape
+    nk, hkv, dv = v.shape
+    scale = 1.0 / np.sqrt(dqk) if scale is None else float(scale)
+    dq, dk, dvv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    dsink = np.empty(hq)
+    rc = lib.oracle_sink_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(qpos), _ptr(kpos),
+                                       _ptr(sink), _ptr(dout), nq, nk, hq, hkv, dqk, dv,
+                                       int(window), scale, _ptr(dq), _ptr(dk), _ptr(dvv),
+                                       _ptr(dsink))
+    if rc != 0:
+        raise ValueError("oracle_sink_attention_bwd failed (%d)" % rc)
+    return dq, dk, dvv, dsink
 
 
 def rope_partial(x, pos, base: float, rope_dim: int = 64, style: int = 0, lib=None):

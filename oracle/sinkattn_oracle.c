@@ -218,3 +218,115 @@ void oracle_round_bf16(const double *x, uint16_t *out, int64_t n) {
         out[i] = sign | (uint16_t)((bits >> 16) & 0x7FFFu);
     }
 }
+
+/*
+ * Gradients of oracle_sink_attention for an upstream gradient dout of the loss
+ * with respect to o (same layout as o).  Derived from the Section 2.2
+ * definitions by the chain rule, with s_ij = e^(a_ij) / Z_i,
+ * Z_i = e^(sink) + sum_j e^(a_ij) and p_i = e^(sink) / Z_i (the sink's share):
+ *   dv_j   += sum_i s_ij dout_i                          (o_i = sum_j s_ij v_j)
+ *   dP_ij   = dout_i . v_j,   D_i = sum_j s_ij dP_ij = dout_i . o_i
+ *   dA_ij   = s_ij (dP_ij - D_i)                          (softmax over J_i + sink)
+ *   dq_i    = scale sum_j dA_ij k_j,   dk_j += scale sum_i dA_ij q_i
+ *   dsink_h = - sum_i p_i D_i   (the sink column has no value, so its dP is 0)
+ * dk and dv sum over the query heads of the KV group.  Outputs are overwritten:
+ *   dq [nq, hq, dqk]   dk [nk, hkv, dqk]   dv [nk, hkv, dv]   dsink [hq]
+ * Plain loops in fp64; the forward weights are recomputed.  Returns 0 / -1.
+ */
+int oracle_sink_attention_bwd(const double *q, const double *k, const double *v,
+                              const int64_t *qpos, const int64_t *kpos,
+                              const double *sink, const double *dout, int64_t nq,
+                              int64_t nk, int hq, int hkv, int dqk, int dv,
+                              int64_t window, double scale, double *dq, double *dk,
+                              double *dvv, double *dsink) {
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || dqk <= 0 || dv <= 0 || nq < 0 ||
+        nk < 0)
+        return -1;
+    const int group = hq / hkv;
+    memset(dq, 0, sizeof(double) * (size_t)(nq * hq * dqk));
+    memset(dk, 0, sizeof(double) * (size_t)(nk * hkv * dqk));
+    memset(dvv, 0, sizeof(double) * (size_t)(nk * hkv * dv));
+    for (int h = 0; h < hq; ++h)
+        dsink[h] = 0.0;
+    int bad = 0;
+
+    /* one KV group per iteration: its dk / dv rows and its heads' dq / dsink
+     * are written by that iteration only */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int g = 0; g < hkv; ++g) {
+        double *a = (double *)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+        double *s = (double *)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+        double *oi = (double *)malloc(sizeof(double) * (size_t)dv);
+        char *vis = (char *)malloc((size_t)(nk > 0 ? nk : 1));
+        if (!a || !s || !oi || !vis) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+            for (int h = g * group; h < (g + 1) * group; ++h) {
+                for (int64_t i = 0; i < nq; ++i) {
+                    const double *qi = q + (i * hq + h) * dqk;
+                    const double *di = dout + (i * hq + h) * dv;
+                    double m = sink[h];
+                    for (int64_t j = 0; j < nk; ++j) {
+                        const int64_t dp = qpos[i] - kpos[j];
+                        vis[j] = (kpos[j] >= 0) && (dp >= 0) && (window <= 0 || dp < window);
+                        if (!vis[j])
+                            continue;
+                        const double *kj = k + (j * hkv + g) * dqk;
+                        double dot = 0.0;
+                        for (int c = 0; c < dqk; ++c)
+                            dot += qi[c] * kj[c];
+                        a[j] = dot * scale;
+                        if (a[j] > m)
+                            m = a[j];
+                    }
+                    double z = (sink[h] == -INFINITY) ? 0.0 : exp(sink[h] - m);
+                    for (int64_t j = 0; j < nk; ++j)
+                        if (vis[j])
+                            z += exp(a[j] - m);
+                    if (!(z > 0.0))
+                        continue; /* nothing visible and no sink: o = 0, no gradient */
+                    const double p_sink = (sink[h] == -INFINITY) ? 0.0 : exp(sink[h] - m) / z;
+                    for (int c = 0; c < dv; ++c)
+                        oi[c] = 0.0;
+                    for (int64_t j = 0; j < nk; ++j) {
+                        if (!vis[j])
+                            continue;
+                        s[j] = exp(a[j] - m) / z;
+                        const double *vj = v + (j * hkv + g) * dv;
+                        for (int c = 0; c < dv; ++c)
+                            oi[c] += s[j] * vj[c];
+                    }
+                    double D = 0.0;
+                    for (int c = 0; c < dv; ++c)
+                        D += di[c] * oi[c];
+                    dsink[h] -= p_sink * D;
+                    double *dqi = dq + (i * hq + h) * dqk;
+                    for (int64_t j = 0; j < nk; ++j) {
+                        if (!vis[j])
+                            continue;
+                        const double *vj = v + (j * hkv + g) * dv;
+                        const double *kj = k + (j * hkv + g) * dqk;
+                        double *dvj = dvv + (j * hkv + g) * dv;
+                        double *dkj = dk + (j * hkv + g) * dqk;
+                        double dP = 0.0;
+                        for (int c = 0; c < dv; ++c) {
+                            dP += di[c] * vj[c];
+                            dvj[c] += s[j] * di[c];
+                        }
+                        const double dA = s[j] * (dP - D);
+                        for (int c = 0; c < dqk; ++c) {
+                            dqi[c] += scale * dA * kj[c];
+                            dkj[c] += scale * dA * qi[c];
+                        }
+                    }
+                }
+            }
+        }
+        free(a);
+        free(s);
+        free(oi);
+        free(vis);
+    }
+    return bad ? -1 : 0;
+}

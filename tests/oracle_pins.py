@@ -355,4 +355,95 @@ def pin_bf16_rounding(lib):
     assert (int(nan[0]) & 0x7F80) == 0x7F80 and (int(nan[0]) & 0x7F) != 0
 
 
+# ----------------------------------------------------------------------------- backward
+
+def _bwd(lib, q, k, v, sink, dout, window, scale=None, qpos=None, kpos=None):
+    T = q.shape[0]
+    qpos = np.arange(T) if qpos is None else qpos
+    kpos = np.arange(k.shape[0]) if kpos is None else kpos
+    return oracle.sink_attention_bwd(q, k, v, qpos, kpos, sink, dout, window, scale, lib=lib)
+
+
+def _loss(lib, q, k, v, sink, dout, window):
+    o, _ = _run(lib, q, k, v, sink, window)
+    return float((o * dout).sum())
+
+
+def pin_bwd_finite_differences(lib):
+    """Every gradient against central differences of the forward oracle's loss
+    L = sum(dout * o) (fp64, h = 1e-6): windowed and global, a -inf sink head."""
+    for window, seed in ((4, 0), (0, 1)):
+        rng = _rng(40 + seed)
+        T, Hq, Hkv, d, dv = 6, 4, 2, 5, 3
+        q = rng.standard_normal((T, Hq, d))
+        k = rng.standard_normal((T, Hkv, d))
+        v = rng.standard_normal((T, Hkv, dv))
+        sink = np.array([0.3, -1.2, -np.inf, 1.7])
+        dout = rng.standard_normal((T, Hq, dv))
+        dq, dk, dvv, dsink = _bwd(lib, q, k, v, sink, dout, window)
+        h = 1e-6
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dvv), ("sink", sink, dsink)):
+            flat, gflat = x.reshape(-1), g.reshape(-1)
+            for idx in range(flat.size):
+                if not np.isfinite(flat[idx]):
+                    assert gflat[idx] == 0.0, (name, idx)
+                    continue
+                keep = flat[idx]
+                flat[idx] = keep + h
+                lp = _loss(lib, q, k, v, sink, dout, window)
+                flat[idx] = keep - h
+                lm = _loss(lib, q, k, v, sink, dout, window)
+                flat[idx] = keep
+                fd = (lp - lm) / (2 * h)
+                assert abs(fd - gflat[idx]) <= 1e-6 * (1 + abs(fd)), (name, idx, fd, gflat[idx])
+
+
+def pin_bwd_torch_autograd(lib):
+    """Against torch autograd (fp64) of the augmented softmax written with
+    library ops: logits with an extra sink column, softmax, drop the column."""
+    rng = _rng(50)
+    T, Hq, Hkv, d, dv, window = 9, 4, 1, 6, 5, 5
+    q = rng.standard_normal((T, Hq, d))
+    k = rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, dv))
+    sink = rng.standard_normal(Hq)
+    dout = rng.standard_normal((T, Hq, dv))
+    scale = 1.0 / math.sqrt(d)
+    tq, tk, tv, ts = (torch.tensor(x, requires_grad=True) for x in (q, k, v, sink))
+    kk = tk.repeat_interleave(Hq // Hkv, 1)
+    vv = tv.repeat_interleave(Hq // Hkv, 1)
+    logits = torch.einsum("ihc,jhc->hij", tq, kk) * scale
+    i = torch.arange(T).view(T, 1)
+    j = torch.arange(T).view(1, T)
+    vis = (j <= i) & (i - j < window)
+    logits = logits.masked_fill(~vis, float("-inf"))
+    aug = torch.cat([logits, ts.view(Hq, 1, 1).expand(Hq, T, 1)], 2)
+    p = torch.softmax(aug, 2)[:, :, :T]
+    o = torch.einsum("hij,jhc->ihc", p, vv)
+    (o * torch.from_numpy(dout)).sum().backward()
+    got = _bwd(lib, q, k, v, sink, dout, window)
+    for g, t in zip(got, (tq, tk, tv, ts)):
+        assert np.allclose(g, t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def pin_bwd_no_sink_matches_softmax_attention(lib):
+    """sink = -inf: dsink = 0 and dq, dk, dv are those of plain causal softmax
+    attention (torch SDPA autograd, fp64)."""
+    rng = _rng(60)
+    T, Hq, Hkv, d, dv = 7, 2, 2, 4, 3
+    q = rng.standard_normal((T, Hq, d))
+    k = rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, dv))
+    dout = rng.standard_normal((T, Hq, dv))
+    sink = np.full(Hq, -np.inf)
+    tq, tk, tv = (torch.tensor(x.transpose(1, 0, 2).copy(), requires_grad=True)
+                  for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    (o * torch.from_numpy(dout.transpose(1, 0, 2).copy())).sum().backward()
+    dq, dk, dvv, dsink = _bwd(lib, q, k, v, sink, dout, 0)
+    assert np.all(dsink == 0.0)
+    for g, t in zip((dq, dk, dvv), (tq, tk, tv)):
+        assert np.allclose(g, t.grad.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

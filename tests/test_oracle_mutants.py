@@ -33,6 +33,13 @@ MUTATIONS = {
     "rope_pairs_swapped_style": ("const int i0 = style == 0 ? 2 * c : c;",
                                  "const int i0 = style == 1 ? 2 * c : c;"),
     "bf16_truncates": ("nearbyint(ldexp(a, -ulp_exp))", "floor(ldexp(a, -ulp_exp))"),
+    "bwd_softmax_term_dropped": ("const double dA = s[j] * (dP - D);",
+                                 "const double dA = s[j] * dP;"),
+    "bwd_dsink_sign": ("dsink[h] -= p_sink * D;", "dsink[h] += p_sink * D;"),
+    "bwd_dq_scale_missing": ("dqi[c] += scale * dA * kj[c];", "dqi[c] += dA * kj[c];"),
+    "bwd_dv_weight_missing": ("dvj[c] += s[j] * di[c];", "dvj[c] += di[c];"),
+    "bwd_D_without_output": ("D += di[c] * oi[c];", "D += di[c];"),
+    "bwd_sink_share_unnormalised": ("exp(sink[h] - m) / z;", "exp(sink[h] - m);"),
 }
 
 
