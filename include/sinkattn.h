@@ -139,6 +139,32 @@ int sinkattn_prefill_global_rope(const void *q, const void *k, const void *v, co
                                  double rope_base, int dtype, void *stream);
 
 /*
+ * Backward of a causal prefill (sinkattn_prefill_swa with window >= 1, or
+ * sinkattn_prefill_global with window = 0): gradients of the loss with respect
+ * to q, k, v and the sink logits, given the upstream gradient dout of o.
+ * From Section 2.2 by the chain rule, with lse_i the forward log-normaliser
+ * (ln of e^sink + sum_j e^(a_ij)), s_ij = e^(a_ij - lse_i), D_i = dout_i . o_i:
+ *   dS_ij = s_ij (dout_i . v_j - D_i),  dq_i = scale sum_j dS_ij k_j,
+ *   dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i s_ij dout_i  (dk, dv summed over
+ *   the query heads of the KV head),  dsink_h = -sum_i e^(sink_h - lse_i) D_i
+ *   (summed over every token of every sequence).
+ *   q, k, v, o, dout: bf16, layouts of the prefill (o, lse: the forward's outputs
+ *   for these inputs; pass lse from the forward call with return of lse).
+ *   dq [B,T,Hq,192], dk [B,T,Hkv,192], dv [B,T,Hkv,128], dsink [Hq]: fp32,
+ *   overwritten.  Gradients are with respect to the q and k the attention saw
+ *   (after RoPE).  workspace: sinkattn_backward_workspace_bytes(B, T, Hq)
+ *   bytes.  Deterministic (no atomics).  Supported: bf16 (UNSUPPORTED
+ *   otherwise); outputs and workspace must not overlap each other or inputs.
+ */
+size_t sinkattn_backward_workspace_bytes(int B, int T, int Hq);
+
+int sinkattn_backward(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, const float *sink, float *dq,
+                      float *dk, float *dv, float *dsink, int B, int T, int Hq, int Hkv, int dqk,
+                      int dv_dim, int window, float scale, void *workspace, size_t ws_bytes,
+                      int dtype, void *stream);
+
+/*
  * Bytes of fp32 workspace that sinkattn_decode / sinkattn_verify need for a
  * split-K pass over a contiguous cache with at most `max_splits` splits:
  * B * n_q * Hq * max_splits * (dv + 2) * 4.  Zero if max_splits <= 1.

@@ -75,7 +75,8 @@ int prefill_common(const void *q, const void *k, const void *v, const float *sin
         return SINKATTN_ERR_NULL_PTR;
     if (B < 0 || T < 0)
         return SINKATTN_ERR_SHAPE;
-    if ((int64_t)B * T * Hq > INT_MAX || (int64_t)B * T > INT_MAX / kDqk)
+    if ((int64_t)B * T * Hq > INT_MAX || (int64_t)B * T > INT_MAX / kDqk ||
+        (int64_t)T * Hq * kDqk * 4 > INT_MAX)  // one sequence's rows: 32-bit offsets
         return SINKATTN_ERR_SHAPE;
     const size_t es = esize(dtype);
     const size_t qn = (size_t)B * T * Hq * kDqk * es, kn = (size_t)B * T * Hkv * kDqk * es;
@@ -374,6 +375,56 @@ int sinkattn_prefill_global_rope(const void *q, const void *k, const void *v, co
     a.rope_q = 1;
     a.rope_base = rope_base;
     return status_from_hip(launch_prefill_bf16(a, s));
+}
+
+size_t sinkattn_backward_workspace_bytes(int B, int T, int Hq) {
+    if (B <= 0 || T <= 0 || Hq <= 0)
+        return 0;
+    return 2 * (size_t)B * T * Hq * sizeof(float);
+}
+
+int sinkattn_backward(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, const float *sink, float *dq,
+                      float *dk, float *dv, float *dsink, int B, int T, int Hq, int Hkv, int dqk,
+                      int dv_dim, int window, float scale, void *workspace, size_t ws_bytes,
+                      int dtype, void *stream) {
+    int st = check_heads(Hq, Hkv, dqk, dv_dim, dtype);
+    if (st)
+        return st;
+    if (dtype != SINKATTN_BF16)
+        return SINKATTN_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !o || !dout || !lse || !sink || !dq || !dk || !dv || !dsink)
+        return SINKATTN_ERR_NULL_PTR;
+    if (B < 0 || T < 0 || window < 0)
+        return SINKATTN_ERR_SHAPE;
+    if ((int64_t)B * T * Hq > INT_MAX || (int64_t)B * T > INT_MAX / kDqk ||
+        (int64_t)T * Hq * kDqk * 4 > INT_MAX)
+        return SINKATTN_ERR_SHAPE;
+    const size_t need = sinkattn_backward_workspace_bytes(B, T, Hq);
+    if (need > 0 && (!workspace || ws_bytes < need))
+        return SINKATTN_ERR_WORKSPACE;
+    const size_t n = (size_t)B * T;
+    const size_t qn = n * Hq * kDqk * 2, kn = n * Hkv * kDqk * 2, vn = n * Hkv * kDv * 2;
+    const size_t on = n * Hq * kDv * 2, ln = n * Hq * 4;
+    const size_t dqn = n * Hq * kDqk * 4, dkn = n * Hkv * kDqk * 4, dvn = n * Hkv * kDv * 4;
+    const void *ins[7] = {q, k, v, o, dout, lse, sink};
+    const size_t insz[7] = {qn, kn, vn, on, on, ln, (size_t)Hq * 4};
+    const void *outs[5] = {dq, dk, dv, dsink, workspace};
+    const size_t outsz[5] = {dqn, dkn, dvn, (size_t)Hq * 4, need};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 7; ++j)
+            if (overlaps(outs[i], outsz[i], ins[j], insz[j]))
+                return SINKATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(outs[i], outsz[i], outs[j], outsz[j]))
+                return SINKATTN_ERR_ALIAS;
+    }
+    if (n == 0)
+        return SINKATTN_OK;
+    BwdArgs a{q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, (float *)workspace,
+              (float *)workspace + n * Hq, B, T, Hq, Hkv, window,
+              scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)dqk))};
+    return status_from_hip(launch_backward(a, (hipStream_t)stream));
 }
 
 size_t sinkattn_decode_workspace_bytes(int B, int Hq, int dv, int n_q, int max_splits) {

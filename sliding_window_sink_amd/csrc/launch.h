@@ -49,6 +49,16 @@ struct AppendArgs {
     float k_scale = 1.f, v_scale = 1.f;
 };
 
+// Gradients of a causal prefill (positions 0..T-1, window <= 0: global).
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;  // bf16, layouts as the prefill's
+    const float *lse, *sink;           // forward lse [B,Hq,T] (natural log), sinks [Hq]
+    float *dq, *dk, *dv, *dsink;       // fp32 outputs
+    float *D, *PS;                     // workspace, [B,Hq,T] each
+    int B, T, Hq, Hkv, window;
+    float scale;
+};
+
 // Clamp a device-side cached length into the range the host validated.
 __device__ __forceinline__ int clamp_len(int len, int max_len) {
     return len < 0 ? 0 : (len > max_len ? max_len : len);
@@ -76,6 +86,8 @@ hipError_t launch_cached_f32(const CachedArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int bf16, hipStream_t s);
 hipError_t launch_advance_len(int32_t *cache_len, const int32_t *n_accept, int B, int n,
                               hipStream_t s);
+
+hipError_t launch_backward(const BwdArgs &a, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -61,6 +61,9 @@ def _bind(lib):
                              i32, f32, i32, p, sz, i32, p], i32),
         "sinkattn_kv_append": ([p, p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, i32, p], i32),
         "sinkattn_advance_len": ([p, p, i32, i32, p], i32),
+        "sinkattn_backward_workspace_bytes": ([i32, i32, i32], sz),
+        "sinkattn_backward": ([p, p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+                               f32, p, sz, i32, p], i32),
         "sinkattn_decode_fp8": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32,
                                  i32, f32, f32, f32, i32, f64, i32, p, sz, p], i32),
         "sinkattn_verify_fp8": ([p, p, p, p, p, i32, i32, p, i32, p, p, p, i32, i32, i32, i32,
@@ -100,7 +103,7 @@ EXPORTED = ["sinkattn_abi_version", "sinkattn_status_string", "sinkattn_rope_par
             "sinkattn_decode", "sinkattn_verify", "sinkattn_kv_append",
             "sinkattn_prefill_global_rope", "sinkattn_decode_rope", "sinkattn_verify_rope",
             "sinkattn_advance_len", "sinkattn_decode_fp8", "sinkattn_verify_fp8",
-            "sinkattn_kv_append_fp8"]
+            "sinkattn_kv_append_fp8", "sinkattn_backward_workspace_bytes", "sinkattn_backward"]
 
 
 def _check(rc: int):
@@ -407,6 +410,33 @@ def kv_append_fp8(k_new, v_new, k_cache, v_cache, cache_len, kind=RING, n_accept
                                         int(kind), k_cache.shape[2], _ptr(cache_len),
                                         _ptr(n_accept), B, n, Hkv, dqk, v_new.shape[3],
                                         float(k_scale), float(v_scale), _stream()))
+
+
+def backward(q, k, v, o, dout, lse, sink, window: int = 0, scale=None, workspace=None,
+             out=None):
+    """Gradients (dq, dk, dv, dsink), fp32, of the causal prefill that produced o
+    and lse (window >= 1: SWA, 0: global) for the upstream gradient dout."""
+    _dev(q, k, v, o, dout, lse, sink, workspace)
+    B, T, Hq, dqk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    for t in (q, k, v, o, dout):
+        if t.dtype != torch.bfloat16:
+            raise SinkAttnError(-3, "q, k, v, o, dout are bfloat16")
+    if o.shape != (B, T, Hq, dv) or dout.shape != o.shape or lse.shape != (B, Hq, T):
+        raise SinkAttnError(-2, "o / dout / lse shapes disagree")
+    need = int(lib().sinkattn_backward_workspace_bytes(B, T, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dvv, dsink = out if out is not None else (
+        torch.empty(B, T, Hq, dqk, **f32), torch.empty(B, T, Hkv, dqk, **f32),
+        torch.empty(B, T, Hkv, dv, **f32), torch.empty(Hq, **f32))
+    _check(lib().sinkattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(sink), _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(dsink), B, T,
+                                   Hq, Hkv, dqk, dv, int(window), _scale(scale), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _dtype_code(q), _stream()))
+    return dq, dk, dvv, dsink
 
 
 def advance_len(cache_len, n, n_accept=None):

@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(ops.EXPORTED) == names
@@ -196,6 +196,25 @@ def test_fp8_validation(lib):
              1.0, None) == SHAPE
     assert a(FAKE[0], FAKE[1], FAKE[2], FAKE[3], 0, 128, FAKE[4], None, 0, 4, 8, 192, 128, 1.0,
              1.0, None) == OK
+
+
+def test_backward_validation(lib):
+    ws_need = lib.sinkattn_backward_workspace_bytes(1, 64, 16)
+    assert ws_need == 2 * 64 * 16 * 4
+    def bwd(dtype=1, window=128, ws=FAKE[11], ws_bytes=ws_need, dq=FAKE[7], T=64, Hq=16,
+            lse=FAKE[5]):
+        return lib.sinkattn_backward(FAKE[0], FAKE[1], FAKE[2], FAKE[3], FAKE[4], lse, FAKE[6],
+                                     dq, FAKE[8], FAKE[9], FAKE[10], 1, T, Hq, 2, 192, 128,
+                                     window, 0.0, ws, ws_bytes, dtype, None)
+    assert bwd(dtype=0) == UNSUP
+    assert bwd(lse=None) == NULL
+    assert bwd(window=-1) == SHAPE
+    assert bwd(Hq=15) == SHAPE
+    assert bwd(ws=None) == WS
+    assert bwd(ws_bytes=ws_need - 4) == WS
+    assert bwd(dq=P(FAKE[0].value + 64)) == ALIAS      # dq over q
+    assert bwd(dq=P(FAKE[8].value + 64)) == ALIAS      # dq over dk
+    assert bwd(T=0, ws=None, ws_bytes=0) == OK
 
 
 def test_rope_and_append_validation(lib):
