@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--prewarm-s", type=float, default=1.0,
                    help="untimed seconds of steps before the warm-up steps (clock ramp)")
-    p.add_argument("--only", default="", help="comma list of: swa,global,decode,verify,spec")
+    p.add_argument("--only", default="", help="comma list of: swa,global,decode,verify,spec,backward")
     p.add_argument("--counter-pass", action="store_true",
                    help="for rocprofv3 --pmc runs: one 1 GiB device copy (the calibration "
                         "kernel of known traffic), then 3 launches of the headline kernel")
@@ -226,6 +226,45 @@ def run_global_prefill(torch, ops, synth, dev, reps=5):
                 kernel_ms=kms, tflops_kernel=flops / kms / 1e9,
                 mfma_frac_kernel=flops / kms / 1e9 / PEAK_BF16_TFLOPS,
                 unfused_rope_ms=rms, unfused_step_ms=kms + rms, flops=flops)
+
+
+BWD_FLOP_PER_PAIR_HEAD = 2 * (192 + 128 + 128 + 192 + 192)  # S, dP, dV, dK, dQ products
+
+
+def run_backward(torch, ops, synth, dev, reps=5):
+    """Backward of the SWA (T=32768, 64/8 heads, W=128) and global (T=32768,
+    64/4 heads) prefill layers: dq, dk, dv and dsink from q, k, v, the forward's
+    o and lse, and an N(0,1) upstream gradient.  Algorithmic FLOPs: the five
+    products of each visible (query, key, head) -- S, dP, dV, dK, dQ."""
+    out = {}
+    for wid, name in ((2, "swa"), (3, "global")):
+        w = synth.WORKLOADS[wid]
+        B, T, Hq, Hkv = w.B, w.T, w.Hq, w.Hkv
+        window = w.window if wid == 2 else 0
+        q = synth.device_normal(w.seed, (B, T, Hq, 192), device=dev)
+        k = synth.device_normal(w.seed + 1, (B, T, Hkv, 192), device=dev)
+        v = synth.device_normal(w.seed + 2, (B, T, Hkv, 128), device=dev)
+        sink = synth.device_normal(w.seed + 3, (Hq,), torch.float32, device=dev)
+        dout = synth.device_normal(w.seed + 4, (B, T, Hq, 128), device=dev)
+        if window:
+            o, lse = ops.prefill_swa(q, k, v, sink, window=window, return_lse=True)
+        else:
+            o, lse = ops.prefill_global(q, k, v, sink, return_lse=True)
+        grads = ops.backward(q, k, v, o, dout, lse, sink, window)  # warm-up, allocates outputs
+        ws = torch.empty(ops.lib().sinkattn_backward_workspace_bytes(B, T, Hq) // 4,
+                         dtype=torch.float32, device=dev)
+        t = Timer(torch)
+        for _ in range(reps):
+            with t:
+                ops.backward(q, k, v, o, dout, lse, sink, window, workspace=ws, out=grads)
+        ms = t.mean_ms()
+        pairs = (swa_pairs(T, window) if window else global_pairs(T)) * B
+        flops = pairs * Hq * BWD_FLOP_PER_PAIR_HEAD
+        out[name] = dict(workload="backward_%s_bf16_T%d_%dq%dkv" % (name, T, Hq, Hkv),
+                         ms=ms, tflops=flops / ms / 1e9,
+                         mfma_frac=flops / ms / 1e9 / PEAK_BF16_TFLOPS, flops=flops)
+        del q, k, v, dout, o, lse, grads, ws
+    return out
 
 
 def _graph_time(torch, fn, reps=20):
@@ -603,7 +642,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     only = set(args.only.split(",")) if args.only else {"swa", "global", "decode", "verify",
-                                                                "spec"}
+                                                                "spec", "backward"}
 
     if args.counter_pass:
         # calibration: a plain copy moves exactly 1 GiB in and 1 GiB out
@@ -665,6 +704,9 @@ def main():
             others["hybrid_decode_fp8"] = run_hybrid_decode(torch, ops, synth, dev, fp8=True)
             others["hybrid_decode_fp8"]["speedup_vs_bf16"] = (
                 others["hybrid_decode"]["step_ms"] / others["hybrid_decode_fp8"]["step_ms"])
+        if "backward" in only:
+            log("[bench] backward (SWA and global layers, T=32768)")
+            others["backward"] = run_backward(torch, ops, synth, dev)
         if "spec" in only:
             log("[bench] self-speculative step B=64 ctx 16384")
             others["spec_loop"] = run_spec_loop(torch, ops, synth, dev)
