@@ -53,6 +53,7 @@ def _forward(q, k, v, sink, window):
     (2, 97, 8, 1, 128),
     (1, 300, 16, 2, 128),
     (1, 150, 32, 2, 0),     # global, 16 heads per KV head (two dq workgroups)
+    (1, 700, 8, 1, 512),    # W = 512 (the report's Table 2 ablation width)
 ])
 def test_backward_vs_oracle(B, T, Hq, Hkv, window):
     _print_case("backward", B, T, Hq, Hkv, window)
@@ -75,6 +76,30 @@ def test_backward_vs_oracle(B, T, Hq, Hkv, window):
         ref_dsink += rs
     assert_close(dsink, ref_dsink, torch.bfloat16, "dsink")
     assert dsink[1].item() == 0.0  # a -inf sink takes no mass and gets no gradient
+
+
+@pytest.mark.parametrize("sink_val,window", [(8.0, 128), (8.0, 0), (1e3, 128)])
+def test_backward_sink_stress(sink_val, window):
+    """A dominant sink (+8: most of the mass, so dsink carries most of the
+    gradient) and an absorbing one (1e3: o = 0, so every gradient is exactly 0)."""
+    _print_case("backward sink stress", sink_val, window)
+    B, T, Hq, Hkv = 1, 260, 8, 1
+    q, k, v, _ = synth.prefill_inputs(1234, B, T, Hq, Hkv, torch.bfloat16)
+    sink = torch.full((Hq,), sink_val, dtype=torch.float32)
+    dout = synth.normal(synth.generator(4321), (B, T, Hq, 128))
+    qd, kd, vd, sd, gd = (t.to(DEV) for t in (q, k, v, sink, dout))
+    o, lse = _forward(qd, kd, vd, sd, window)
+    dq, dk, dv, dsink = ops.backward(qd, kd, vd, o, gd, lse, sd, window)
+    torch.cuda.synchronize()
+    if sink_val == 1e3:
+        for x in (dq, dk, dv, dsink):
+            assert torch.count_nonzero(x) == 0
+        return
+    pos = np.arange(T)
+    rq, rk, rv, rs = oracle.sink_attention_bwd(q[0], k[0], v[0], pos, pos, sink, dout[0], window)
+    for name, got, ref in (("dq", dq[0], rq), ("dk", dk[0], rk), ("dv", dv[0], rv),
+                           ("dsink", dsink, rs)):
+        assert_close(got, ref, torch.bfloat16, name)
 
 
 def test_backward_deterministic():
