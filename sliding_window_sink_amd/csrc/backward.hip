@@ -21,15 +21,18 @@
 //                    the forward's layout -- S^T = K Q^T with each lane owning a
 //                    query column, K rows permuted so C-register i of half hh is
 //                    key 16hh + i; dP^T = V dO^T with V rows permuted the same
-//                    way; dQ^T += K^T dS^T with K^T staged in LDS in key order.
+//                    way; dQ^T += K^T dS^T with the K^T operand read from the
+//                    same K rows by gfx950's transposing LDS loads.
 //   bwd_dkdv_kernel  per (KV group, 32-key block), 4 waves: S = Q K^T with each
 //                    lane owning a key column and Q rows permuted so C-register i
 //                    of half hh is query 16hh + i, so P and dS are directly the
-//                    B operands of dV^T += dO^T P and dK^T += Q^T dS; Q^T and
-//                    dO^T go through a per-wave LDS tile; the 4 waves (disjoint
+//                    B operands of dV^T += dO^T P and dK^T += Q^T dS; Q and dO
+//                    rows go to a per-wave row-major LDS tile whose transposing
+//                    reads give the Q^T / dO^T operands; the 4 waves (disjoint
 //                    heads) are summed through LDS in a fixed order at the end.
 // Every output element is written once (no atomics): results are deterministic.
 #include "common.h"
+#include "lds_tr.h"
 
 namespace sinkattn {
 namespace {
@@ -99,14 +102,12 @@ constexpr int kQWaves = 8;
 constexpr int kQThreads = kQWaves * 64;
 constexpr int kKPitch = kDqk + 8;   // K rows in LDS (bf16)
 constexpr int kVPitch = kDv + 8;    // V rows in LDS (bf16)
-constexpr int kTPitch = kKb + 8;    // K^T rows in LDS (bf16): 80 bytes, 16-byte aligned
 constexpr int kKChunks = kKb * kDqk / 8;  // 768 16-byte pieces of a K block
 constexpr int kVChunks = kKb * kDv / 8;   // 512
 
 struct DqSmem {
     uint16_t k[2][kKb * kKPitch];
     uint16_t v[2][kKb * kVPitch];
-    uint16_t kt[2][kDqk * kTPitch];
 };
 
 struct DqStaged {
@@ -183,10 +184,6 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
             const int c = tid + u * kQThreads;
             const int key = c / 24, d0 = (c % 24) * 8;
             *(uint4 *)&sm.k[buf][row_of_key(key) * kKPitch + d0] = st.k[u];
-            const uint32_t w[4] = {st.k[u].x, st.k[u].y, st.k[u].z, st.k[u].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sm.kt[buf][(d0 + e) * kTPitch + key] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
         }
         *(uint4 *)&sm.v[buf][row_of_key(tid / 16) * kVPitch + (tid % 16) * 8] = st.v;
     };
@@ -195,6 +192,18 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
 #pragma unroll
     for (int db = 0; db < kDqk / 32; ++db)
         acc[db] = f32x16{};
+
+    // K^T operand of dQ^T += K^T dS^T through transposing reads of the K rows: in
+    // lane group G = lane/16, source lane 4e'+q points at key 16hh + 8t + 4L + e'
+    // (row row_of_key of the staged tile) and dims 32d + 16(G%2) + 4q .. +3, so
+    // A-row r holds dim 32d + r and element 4L + e' holds key 16hh + 8t + 4L + e'.
+    int kt_off[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int L = 0; L < 2; ++L)
+            kt_off[t][L] = row_of_key(16 * hh + 8 * t + 4 * L + ((lane & 15) >> 2)) * kKPitch +
+                           16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
     DqStaged st;
     load_block(kb0, st);
@@ -205,7 +214,7 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
 
     for (int j = 0; j < nblk; ++j) {
         const int kb = kb0 + j * kKb;
-        const uint16_t *ks = sm.k[j & 1], *vs = sm.v[j & 1], *kts = sm.kt[j & 1];
+        const uint16_t *ks = sm.k[j & 1], *vs = sm.v[j & 1];
         f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int s = 0; s < kDqk / 16; ++s) {
@@ -231,8 +240,9 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
         for (int d = 0; d < kDqk / 32; ++d)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const uint4 ka = *(const uint4 *)(kts + (32 * d + r) * kTPitch + 16 * hh + 8 * t);
-                acc[d] = mfma32x32x16(as_bf16x8(ka), db_[t], acc[d]);
+                const uint2 lo = lds_tr16(ks + kt_off[t][0] + 32 * d);
+                const uint2 hi = lds_tr16(ks + kt_off[t][1] + 32 * d);
+                acc[d] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), db_[t], acc[d]);
             }
         if (j + 1 < nblk)
             store_block((j + 1) & 1, st);
@@ -260,14 +270,15 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
 
 constexpr int kKWaves = 4;
 constexpr int kKThreads = kKWaves * 64;
-constexpr int kQTPitch = kTq + 8;  // per-wave Q^T / dO^T rows (bf16): 80 bytes
+constexpr int kQRPitch = kDqk + 8;  // per-wave Q rows (bf16): 400 bytes
+constexpr int kGRPitch = kDv + 8;   // per-wave dO rows (bf16): 272 bytes
 constexpr int kRedPitch = kKb + 1;  // fp32 reduction rows
 
 struct DkvSmem {
     union {
         struct {
-            uint16_t qt[kKWaves][kDqk * kQTPitch];
-            uint16_t gt[kKWaves][kDv * kQTPitch];
+            uint16_t qr[kKWaves][kTq * kQRPitch];
+            uint16_t gr[kKWaves][kTq * kGRPitch];
         } w;
         float red[(kDqk + kDv) * kRedPitch];
     };
@@ -321,7 +332,20 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a, int n_un
     const int last = kWindowed ? min(T - 1, kb + kKb - 1 + window - 1) : T - 1;
     const int n_tiles = kb < T ? (last - kb) / kTq + 1 : 0;
     const int qrow_r = key_of_row(r);  // A-row r of a tile holds query q0 + key_of_row(r)
-    uint16_t *qt = sm.w.qt[wave], *gt = sm.w.gt[wave];
+    uint16_t *qt = sm.w.qr[wave], *gt = sm.w.gr[wave];
+    // Q^T / dO^T operands through transposing reads of the row-major tiles: source
+    // lane 4e'+q of group G points at query 16hh + 8t + 4L + e' and dims
+    // 32d + 16(G%2) + 4q .. +3 (A-row r = dim 32d + r)
+    int qt_off[2][2], gt_off[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int L = 0; L < 2; ++L) {
+            const int qq = 16 * hh + 8 * t + 4 * L + ((lane & 15) >> 2);
+            const int dd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            qt_off[t][L] = qq * kQRPitch + dd;
+            gt_off[t][L] = qq * kGRPitch + dd;
+        }
 
     for (int hi = wave; hi < group; hi += kKWaves) {
         const int h = g * group + hi;
@@ -362,24 +386,14 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a, int n_un
                 dd[4 * c + 2] = __builtin_bit_cast(float, d4.z);
                 dd[4 * c + 3] = __builtin_bit_cast(float, d4.w);
             }
-            // Q^T and dO^T of the tile into this wave's LDS, queries in natural order
+            // Q and dO rows of the tile into this wave's LDS, queries in natural order
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int s = 0; s < kDqk / 16; ++s) {
-                const uint32_t w[4] = {qa[s].x, qa[s].y, qa[s].z, qa[s].w};
+            for (int s = 0; s < kDqk / 16; ++s)
+                *(uint4 *)&qt[qrow_r * kQRPitch + (2 * s + hh) * 8] = qa[s];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    qt[((2 * s + hh) * 8 + e) * kQTPitch + qrow_r] =
-                        (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-            }
-#pragma unroll
-            for (int s = 0; s < kDv / 16; ++s) {
-                const uint32_t w[4] = {ga[s].x, ga[s].y, ga[s].z, ga[s].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    gt[((2 * s + hh) * 8 + e) * kQTPitch + qrow_r] =
-                        (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-            }
+            for (int s = 0; s < kDv / 16; ++s)
+                *(uint4 *)&gt[qrow_r * kGRPitch + (2 * s + hh) * 8] = ga[s];
             // S = Q K^T and dP = dO V^T: column = key, register i = query q0 + 16hh + i
             f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -405,15 +419,17 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a, int n_un
             for (int d = 0; d < kDv / 32; ++d)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const uint4 ga2 = *(const uint4 *)(gt + (32 * d + r) * kQTPitch + 16 * hh + 8 * t);
-                    dv[d] = mfma32x32x16(as_bf16x8(ga2), pb[t], dv[d]);
+                    const uint2 lo = lds_tr16(gt + gt_off[t][0] + 32 * d);
+                    const uint2 hi = lds_tr16(gt + gt_off[t][1] + 32 * d);
+                    dv[d] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[t], dv[d]);
                 }
 #pragma unroll
             for (int d = 0; d < kDqk / 32; ++d)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const uint4 qa2 = *(const uint4 *)(qt + (32 * d + r) * kQTPitch + 16 * hh + 8 * t);
-                    dk[d] = mfma32x32x16(as_bf16x8(qa2), sb[t], dk[d]);
+                    const uint2 lo = lds_tr16(qt + qt_off[t][0] + 32 * d);
+                    const uint2 hi = lds_tr16(qt + qt_off[t][1] + 32 * d);
+                    dk[d] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), sb[t], dk[d]);
                 }
         }
     }

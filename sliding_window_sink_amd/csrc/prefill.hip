@@ -27,14 +27,17 @@
 //     per-lane register reductions plus one exchange between wave halves;
 //   - K rows are written into LDS in the order that makes C-register i of lane
 //     half hh hold key 16*hh + i, so P^T feeds the PV MFMA directly as its B
-//     operand, and V is stored transposed ([dim][key]) so its A operand is one
-//     16-byte LDS read per lane.
+//     operand; V rows stay row-major in LDS (one 16-byte write per piece) and
+//     the V^T A operand is read with gfx950's transposing LDS loads (two
+//     ds_read_b64_tr_b16 per MFMA); this replaced a transposed V^T tile built
+//     with 8 scattered 2-byte writes per piece (3-5% of the kernel).
 // Global memory is read through raw buffer descriptors (rows past the end of
 // the sequence read as zero; stores past it are dropped).
 // Workgroup order: blockIdx % units picks (batch, KV group, head half), so on
 // the 8 XCDs of MI355X each XCD sees tiles of the same KV group and the shared
 // K/V blocks hit in its L2.  Global layers run the longest (last) tiles first.
 #include "common.h"
+#include "lds_tr.h"
 
 namespace sinkattn {
 namespace {
@@ -44,23 +47,19 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTq = 32;             // query tokens per tile (MFMA columns)
 constexpr int kKb = 32;             // keys per block (MFMA rows)
 constexpr int kKPitch = kDqk + 8;   // LDS row pitch of K, bf16 elements (400 bytes)
-constexpr int kVPitch = kKb + 8;    // LDS row pitch of V^T, bf16 elements (80 bytes)
+constexpr int kVPitch = kDv + 8;    // LDS row pitch of V rows, bf16 elements (272 bytes)
 constexpr int kKChunks = kKb * kDqk / 8;   // 16-byte pieces of one K block (768)
 constexpr int kVChunks = kKb * kDv / 8;    // 16-byte pieces of one V block (512)
 static_assert(kVChunks == kThreads, "one V piece per thread");
 
 struct PrefillSmem {
     uint16_t k[2][kKb * kKPitch];
-    uint16_t vt[2][kDv * kVPitch];
+    uint16_t v[2][kKb * kVPitch];
 };
 
-// V^T LDS row holding output dim d: the PV accumulator block db, C-row
-// rho = 8a + 4hh + e holds dim 32a + 16(db/2) + 8hh + 4(db%2) + e, so a lane owns
-// runs of 8 consecutive output dims (16-byte stores).
-__device__ __forceinline__ int pv_row_of_dim(int d) {
-    const int a = d >> 5, j = (d >> 4) & 1, hh = (d >> 3) & 1, dbl = (d >> 2) & 1, e = d & 3;
-    return 32 * (2 * j + dbl) + 8 * a + 4 * hh + e;
-}
+// PV accumulator block db, C-row rho = 8a + 4hh + e holds output dim
+// 32a + 16(db/2) + 8hh + 4(db%2) + e, so a lane owns runs of 8 consecutive output
+// dims (16-byte stores); the transposing V reads below pick their dims to match.
 
 struct Staged {
     uint4 k[2];
@@ -126,8 +125,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
     const int nblk = (kend - kb0 + kKb - 1) / kKb;
 
     // Per-thread staging offsets, computed once: K pieces c = tid, tid + 512 (key c/24,
-    // dims (c%24)*8..+7); V piece of v_stage_coords.  Output dim
-    // 8*dc + j sits in V^T row vrow0 + 32*(j/4) + j%4 (see pv_row_of_dim).
+    // dims (c%24)*8..+7); V piece tid (key tid/16, dims (tid%16)*8..+7).
     const bool k2 = tid + kThreads < kKChunks;  // wave-uniform
     uint32_t kg_off[2];
     int kl_off[2];
@@ -137,10 +135,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
         kg_off[u] = (uint32_t)(c / (kDqk / 8)) * krow + kcol + (uint32_t)(c % (kDqk / 8)) * 16;
         kl_off[u] = row_of_key(c / (kDqk / 8)) * kKPitch + (c % (kDqk / 8)) * 8;
     }
-    int v_kk, v_dc;
-    v_stage_coords(tid, v_kk, v_dc);
+    const int v_kk = tid >> 4, v_dc = tid & 15;  // V rows stay row-major in LDS
     const uint32_t vg_off = (uint32_t)v_kk * vrow + vcol + (uint32_t)v_dc * 16;
-    const int vl_off = pv_row_of_dim(v_dc * 8) * kVPitch + v_kk;
+    const int vl_off = v_kk * kVPitch + v_dc * 8;
+    // V^T operand of the PV product read from the row-major V tile with transposing
+    // loads: in group G = lane/16, source lane 4e'+q points at key 16hh + 8t + 4L + e'
+    // and dims d0 = 64(G%2) + 32(q/2) + 16(db/2) + 8(q%2) + 4(db%2), so A-row r holds
+    // dim pv_dim(r) (runs of 8 consecutive output dims per lane, as before).
+    const int vt_lane = (16 * hh + ((lane & 15) >> 2)) * kVPitch + 64 * ((lane >> 4) & 1) +
+                        32 * ((lane & 3) >> 1) + 8 * (lane & 1);
 
     auto load_block = [&](int kb, Staged &st) {
         st.k[0] = buf_load16(kbuf, (uint32_t)kb * krow + kg_off[0]);
@@ -152,11 +155,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
         *(uint4 *)&sm.k[buf][kl_off[0]] = st.k[0];
         if (k2)
             *(uint4 *)&sm.k[buf][kl_off[1]] = st.k[1];
-        const uint32_t w[4] = {st.v.x, st.v.y, st.v.z, st.v.w};
-        uint16_t *vt = &sm.vt[buf][vl_off];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            vt[(32 * (j >> 2) + (j & 3)) * kVPitch] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+        *(uint4 *)&sm.v[buf][vl_off] = st.v;
     };
 
     // Online-softmax state in log2 units, seeded with the sink.
@@ -186,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
         if (j + 2 < nblk)
             load_block(kb + 2 * kKb, cur_next2);
         const uint16_t *ks = sm.k[j & 1];
-        const uint16_t *vs = sm.vt[j & 1];
+        const uint16_t *vs = sm.v[j & 1];
 
         // S^T = K Q^T: rows = keys (permuted so register i <-> key 16*hh + i).
         f32x16 sc = f32x16{};
@@ -238,7 +237,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a, i
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const uint4 va = *(const uint4 *)(vs + (32 * db + r) * kVPitch + 16 * hh + 8 * t);
+                const uint16_t *vp = vs + vt_lane + 8 * t * kVPitch + 16 * (db >> 1) + 4 * (db & 1);
+                const uint2 lo = lds_tr16(vp), hi = lds_tr16(vp + 4 * kVPitch);
+                const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 acc[db] = mfma32x32x16(as_bf16x8(va), pb[t], acc[db]);
             }
 
