@@ -267,6 +267,33 @@ def run_backward(torch, ops, synth, dev, reps=5):
     return out
 
 
+def measured_peaks(torch, dev, reps=10):
+    """The box's own ceilings in this session: a 1 GiB device-to-device copy (torch
+    copy_, read + write bytes / time) and a large bf16 GEMM (torch.matmul, 8192^3 on
+    the vendor BLAS).  Rates of the kernels here are also reported against these."""
+    src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    t = Timer(torch)
+    dst.copy_(src)
+    for _ in range(reps):
+        with t:
+            dst.copy_(src)
+    copy_gbs = 2 * src.numel() * 2 / (t.mean_ms() * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = a @ b
+    t = Timer(torch)
+    for _ in range(reps):
+        with t:
+            torch.matmul(a, b, out=c)
+    gemm_tflops = 2 * n ** 3 / (t.mean_ms() * 1e-3) / 1e12
+    del a, b, c
+    return dict(copy_gbs=round(copy_gbs, 1), gemm_bf16_tflops=round(gemm_tflops, 1),
+                copy="1 GiB int16 torch copy_ (read + write)", gemm="bf16 8192^3 torch.matmul")
+
+
 def _graph_time(torch, fn, reps=20):
     """Capture fn (a sequence of launches) in a HIP graph, replay, time with events."""
     s = torch.cuda.Stream()
@@ -624,9 +651,17 @@ def cpu_baseline(torch, inputs, target_s: float):
             % (T, W, reps)) if n2 == T else \
            ("%d consecutive query tokens (positions %d..%d, 64 heads, W=%d) of the T=%d "
             "SWA prefill incl. RoPE of their q/k rows" % (n2, t0, t0 + n2 - 1, W, T))
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": "%s; %.1f s on the host" % (what, dt),
-            "seconds": dt}
+            "seconds": dt, "cpu_model": model}
 
 
 def main():
@@ -718,6 +753,21 @@ def main():
                 if isinstance(vv, float):
                     v[kk] = round(vv, 5)
     line["other_workloads"] = others
+    if not args.no_others:
+        log("[bench] measured peaks (copy, GEMM)")
+        peaks = measured_peaks(torch, dev)
+        frac = {"swa_prefill_hbm_vs_copy": round(achieved / peaks["copy_gbs"], 4)}
+        if "global_prefill" in others:
+            frac["global_prefill_mfma_vs_gemm"] = round(
+                others["global_prefill"]["tflops_kernel"] / peaks["gemm_bf16_tflops"], 4)
+        if "hybrid_decode" in others:
+            frac["global_decode_hbm_vs_copy"] = round(
+                others["hybrid_decode"]["global_gbs"] / peaks["copy_gbs"], 4)
+        if "verify" in others:
+            frac["global_verify_hbm_vs_copy"] = round(
+                others["verify"]["global_gbs"] / peaks["copy_gbs"], 4)
+        peaks["fractions"] = frac
+        line["measured_peaks"] = peaks
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(torch, inputs, args.cpu_seconds)
