@@ -103,7 +103,6 @@ constexpr int kQThreads = kQWaves * 64;
 constexpr int kKPitch = kDqk + 8;   // K rows in LDS (bf16)
 constexpr int kVPitch = kDv + 8;    // V rows in LDS (bf16)
 constexpr int kKChunks = kKb * kDqk / 8;  // 768 16-byte pieces of a K block
-constexpr int kVChunks = kKb * kDv / 8;   // 512
 
 struct DqSmem {
     uint16_t k[2][kKb * kKPitch];
