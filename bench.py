@@ -46,9 +46,11 @@ def parse():
     p.add_argument("--prewarm-s", type=float, default=1.0,
                    help="untimed seconds of steps before the warm-up steps (clock ramp)")
     p.add_argument("--only", default="", help="comma list of: swa,global,decode,verify,spec,backward")
-    p.add_argument("--counter-pass", action="store_true",
+    p.add_argument("--counter-pass", nargs="?", const="swa", default=None,
+                   choices=["swa", "decode"],
                    help="for rocprofv3 --pmc runs: one 1 GiB device copy (the calibration "
-                        "kernel of known traffic), then 3 launches of the headline kernel")
+                        "kernel of known traffic), then 3 launches of the headline kernel "
+                        "(swa) or of the global layer of the hybrid decode step (decode)")
     return p.parse_args()
 
 
@@ -318,7 +320,7 @@ def _graph_time(torch, fn, reps=20):
 FP8_K_SCALE, FP8_V_SCALE = 0.011, 0.0073  # per-tensor E4M3 scales for N(0,1) K / V
 
 
-def run_hybrid_decode(torch, ops, synth, dev, fp8=False):
+def run_hybrid_decode(torch, ops, synth, dev, fp8=False, counter_pass=False):
     """One decode step of the hybrid block (5 SWA ring layers + 1 global layer) at
     batch 32 over contexts drawn from [16K, 128K]; bf16 caches, or E4M3 caches
     (fp8=True) filled by kv_append_fp8 from the same kind of N(0,1) rows."""
@@ -396,6 +398,11 @@ def run_hybrid_decode(torch, ops, synth, dev, fp8=False):
             swa(r)
         glob()
 
+    if counter_pass:  # 3 eager launches of the global layer for rocprofv3 --pmc
+        for _ in range(3):
+            glob()
+        torch.cuda.synchronize()
+        return dict(kv_bytes_global=int((cl.to(torch.int64) + 1).sum()) * 4 * 640)
     step_ms, _ = _graph_time(torch, block)
     # per-layer times with the caches flushed in between (events around one layer)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -686,8 +693,12 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-        run_swa_prefill(torch, ops, synth, steps=3, warmup=0, dev=dev, prewarm_s=0.0,
-                        fused_only=True)
+        if args.counter_pass == "decode":
+            r = run_hybrid_decode(torch, ops, synth, dev, counter_pass=True)
+            log("[bench] global decode layer: %d KV bytes" % r["kv_bytes_global"])
+        else:
+            run_swa_prefill(torch, ops, synth, steps=3, warmup=0, dev=dev, prewarm_s=0.0,
+                            fused_only=True)
         torch.cuda.synchronize()
         log("[bench] counter pass done")
         return
