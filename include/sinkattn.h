@@ -41,6 +41,14 @@
  *    position p is visible to a query at position P iff P - W < p <= P.
  *  - Supported in this version: dqk == 192, dv == 128 (SINKATTN_ERR_UNSUPPORTED
  *    otherwise); Hq % Hkv == 0.  The bf16 paths need (Hq/Hkv) % 8 == 0.
+ *  - Size limits (SINKATTN_ERR_SHAPE beyond them): B*T*Hq and B*T*dqk below
+ *    2^31; the global prefills, windows over 129 and all fp32 prefills address
+ *    one sequence's q with 32-bit byte offsets, so T*Hq*dqk*(element size) must
+ *    stay below 2^31 (bf16, 64 query heads: T <= 87381); the sliding-window
+ *    bf16 prefills (W <= 129) have no per-sequence limit.
+ *  - A call with nothing to do (B*T == 0 for a prefill or backward; B == 0 for
+ *    decode, verify and advance_len; B*n == 0 for kv_append; n_tok == 0 for
+ *    RoPE) returns SINKATTN_OK with no HIP call; its data pointers may be NULL.
  *  - Calls on different streams that write the same buffers race; nothing else
  *    is shared between calls.
  */
@@ -155,6 +163,8 @@ int sinkattn_prefill_global_rope(const void *q, const void *k, const void *v, co
  *   (after RoPE).  workspace: sinkattn_backward_workspace_bytes(B, T, Hq)
  *   bytes.  Deterministic (no atomics).  Supported: bf16 (UNSUPPORTED
  *   otherwise); outputs and workspace must not overlap each other or inputs.
+ *   B*T == 0: returns at once with no HIP call; no output is written (the
+ *   caller owns the zero dsink of an empty batch).
  */
 size_t sinkattn_backward_workspace_bytes(int B, int T, int Hq);
 

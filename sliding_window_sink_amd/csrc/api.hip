@@ -71,14 +71,17 @@ int prefill_common(const void *q, const void *k, const void *v, const float *sin
     int st = check_heads(Hq, Hkv, dqk, dv, dtype);
     if (st)
         return st;
-    if (!q || !k || !v || !sink || !o)
+    if ((int64_t)B * T != 0 && (!q || !k || !v || !sink || !o))  // empty: may be NULL
         return SINKATTN_ERR_NULL_PTR;
     if (B < 0 || T < 0)
         return SINKATTN_ERR_SHAPE;
-    if ((int64_t)B * T * Hq > INT_MAX || (int64_t)B * T > INT_MAX / kDqk ||
-        (int64_t)T * Hq * kDqk * 4 > INT_MAX)  // one sequence's rows: 32-bit offsets
-        return SINKATTN_ERR_SHAPE;
     const size_t es = esize(dtype);
+    // One sequence's q rows are addressed with 32-bit byte offsets, except by the
+    // persistent sliding-window kernel, which re-bases every run of tiles.
+    const bool rebased = dtype == SINKATTN_BF16 && window > 0 && window <= kSwaMaxWindow;
+    if ((int64_t)B * T * Hq > INT_MAX || (int64_t)B * T > INT_MAX / kDqk ||
+        (!rebased && (int64_t)T * Hq * kDqk * (int64_t)es > INT_MAX))
+        return SINKATTN_ERR_SHAPE;
     const size_t qn = (size_t)B * T * Hq * kDqk * es, kn = (size_t)B * T * Hkv * kDqk * es;
     const size_t vn = (size_t)B * T * Hkv * kDv * es, on = (size_t)B * T * Hq * kDv * es;
     const size_t ln = lse ? (size_t)B * Hq * T * 4 : 0;
@@ -130,7 +133,7 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
     }
     if (kind != SINKATTN_CACHE_RING && kind != SINKATTN_CACHE_CONTIG)
         return SINKATTN_ERR_UNSUPPORTED;
-    if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_len || !sink || !o)
+    if (B != 0 && (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_len || !sink || !o))
         return SINKATTN_ERR_NULL_PTR;
     if (B < 0 || nq < 1 || nq > 8 || cap < 1 || max_len_hint < 0 || num_splits < 0)
         return SINKATTN_ERR_SHAPE;
@@ -273,7 +276,7 @@ int sinkattn_rope_partial(void *x, int dtype, int64_t n_tok, int n_heads, int he
                           void *stream) {
     if (dtype != SINKATTN_F32 && dtype != SINKATTN_BF16)
         return SINKATTN_ERR_DTYPE;
-    if (!x || !pos)
+    if (n_tok != 0 && (!x || !pos))
         return SINKATTN_ERR_NULL_PTR;
     if (n_tok < 0 || n_heads < 0 || head_dim <= 0 || rope_dim < 0 || rope_dim % 2 != 0 ||
         rope_dim > head_dim || !(base > 0.0) || !std::isfinite(base) ||
@@ -305,7 +308,7 @@ int sinkattn_prefill_swa_rope(const void *q, const void *k, const void *v, const
     int st = check_heads(Hq, Hkv, dqk, dv, dtype);
     if (st)
         return st;
-    if (!q || !k || !v || !sink || !o)
+    if ((int64_t)B * T != 0 && (!q || !k || !v || !sink || !o))
         return SINKATTN_ERR_NULL_PTR;
     if (B < 0 || T < 0 || window < 1 || !(rope_base > 0.0) || !std::isfinite(rope_base) ||
         rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > dqk)
@@ -348,16 +351,18 @@ int sinkattn_prefill_global_rope(const void *q, const void *k, const void *v, co
     int st = check_heads(Hq, Hkv, dqk, dv, dtype);
     if (st)
         return st;
-    if (!q || !k || !v || !sink || !o || !k_rot)
+    if ((int64_t)B * T != 0 && (!q || !k || !v || !sink || !o || !k_rot))
         return SINKATTN_ERR_NULL_PTR;
     if (B < 0 || T < 0 || !(rope_base > 0.0) || !std::isfinite(rope_base) || rope_dim < 0 ||
         rope_dim % 2 != 0 || rope_dim > dqk)
         return SINKATTN_ERR_SHAPE;
     if (dtype != SINKATTN_BF16 || rope_dim != 64)
         return SINKATTN_ERR_UNSUPPORTED;
-    if ((int64_t)B * T * Hq > INT_MAX || (int64_t)B * T > INT_MAX / kDqk)
-        return SINKATTN_ERR_SHAPE;
     const size_t es = esize(dtype);
+    // one sequence's q rows are addressed with 32-bit byte offsets
+    if ((int64_t)B * T * Hq > INT_MAX || (int64_t)B * T > INT_MAX / kDqk ||
+        (int64_t)T * Hq * kDqk * (int64_t)es > INT_MAX)
+        return SINKATTN_ERR_SHAPE;
     const size_t qn = (size_t)B * T * Hq * kDqk * es, kn = (size_t)B * T * Hkv * kDqk * es;
     const size_t vn = (size_t)B * T * Hkv * kDv * es, on = (size_t)B * T * Hq * kDv * es;
     const size_t ln = lse ? (size_t)B * Hq * T * 4 : 0;
@@ -400,7 +405,8 @@ int sinkattn_backward(const void *q, const void *k, const void *v, const void *o
         return st;
     if (dtype != SINKATTN_BF16)
         return SINKATTN_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !o || !dout || !lse || !sink || !dq || !dk || !dv || !dsink)
+    if ((int64_t)B * T != 0 &&
+        (!q || !k || !v || !o || !dout || !lse || !sink || !dq || !dk || !dv || !dsink))
         return SINKATTN_ERR_NULL_PTR;
     if (B < 0 || T < 0 || window < 0)
         return SINKATTN_ERR_SHAPE;
@@ -489,7 +495,7 @@ int sinkattn_kv_append(const void *k_new, const void *v_new, void *k_cache, void
         return SINKATTN_ERR_DTYPE;
     if (kind != SINKATTN_CACHE_RING && kind != SINKATTN_CACHE_CONTIG)
         return SINKATTN_ERR_UNSUPPORTED;
-    if (!k_new || !v_new || !k_cache || !v_cache || !cache_len)
+    if ((int64_t)B * n != 0 && (!k_new || !v_new || !k_cache || !v_cache || !cache_len))
         return SINKATTN_ERR_NULL_PTR;
     if (B < 0 || n < 0 || Hkv <= 0 || cap < 1 || dqk <= 0 || dv <= 0)
         return SINKATTN_ERR_SHAPE;
@@ -543,7 +549,7 @@ int sinkattn_kv_append_fp8(const void *k_new, const void *v_new, void *k_cache, 
                            void *stream) {
     if (kind != SINKATTN_CACHE_RING && kind != SINKATTN_CACHE_CONTIG)
         return SINKATTN_ERR_UNSUPPORTED;
-    if (!k_new || !v_new || !k_cache || !v_cache || !cache_len)
+    if ((int64_t)B * n != 0 && (!k_new || !v_new || !k_cache || !v_cache || !cache_len))
         return SINKATTN_ERR_NULL_PTR;
     if (B < 0 || n < 0 || Hkv <= 0 || cap < 1 || dqk <= 0 || dv <= 0 || !(k_scale > 0.f) ||
         !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
@@ -570,7 +576,7 @@ int sinkattn_kv_append_fp8(const void *k_new, const void *v_new, void *k_cache, 
 
 int sinkattn_advance_len(int32_t *cache_len, const int32_t *n_accept, int B, int n,
                          void *stream) {
-    if (!cache_len)
+    if (B != 0 && !cache_len)
         return SINKATTN_ERR_NULL_PTR;
     if (B < 0 || n < 0)
         return SINKATTN_ERR_SHAPE;

@@ -428,9 +428,12 @@ def backward(q, k, v, o, dout, lse, sink, window: int = 0, scale=None, workspace
     if workspace is None:
         workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=q.device)
     f32 = dict(dtype=torch.float32, device=q.device)
+    # dsink of an empty batch is a sum over no tokens: the library writes nothing
+    # then, so a fresh dsink starts at zero in that case
     dq, dk, dvv, dsink = out if out is not None else (
         torch.empty(B, T, Hq, dqk, **f32), torch.empty(B, T, Hkv, dqk, **f32),
-        torch.empty(B, T, Hkv, dv, **f32), torch.empty(Hq, **f32))
+        torch.empty(B, T, Hkv, dv, **f32),
+        torch.zeros(Hq, **f32) if B * T == 0 else torch.empty(Hq, **f32))
     _check(lib().sinkattn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                    _ptr(sink), _ptr(dq), _ptr(dk), _ptr(dvv), _ptr(dsink), B, T,
                                    Hq, Hkv, dqk, dv, int(window), _scale(scale), _ptr(workspace),

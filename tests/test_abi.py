@@ -71,6 +71,11 @@ def test_prefill_validation(lib):
     assert prefill(lib, T=-1) == SHAPE
     assert prefill(lib, B=0) == OK               # nothing to do, no HIP call
     assert prefill(lib, T=0, swa=False) == OK
+    assert prefill(lib, B=0, q=None, o=None) == OK   # empty: pointers may be NULL
+    # one sequence's q must fit 32-bit byte offsets except in the bf16 SWA kernel
+    assert prefill(lib, T=87382, Hq=64, Hkv=8, swa=False) == SHAPE   # 2^31 + 2 bytes of bf16 q
+    assert prefill(lib, T=43691, Hq=64, Hkv=8, dtype=0) == SHAPE     # fp32 SWA
+    assert prefill(lib, T=87382, Hq=64, Hkv=8, window=200) == SHAPE  # window > 129: global kernel
     # o overlapping q
     assert prefill(lib, o=P(FAKE[0].value + 64)) == ALIAS
     assert prefill(lib, lse=P(FAKE[4].value + 8)) == ALIAS
@@ -96,6 +101,7 @@ def test_decode_validation(lib):
     assert decode(lib, max_len=-1) == SHAPE
     assert decode(lib, dtype=2) == DTYPE
     assert decode(lib, B=0) == OK
+    assert decode(lib, B=0, q=None, cache_len=None, o=None) == OK   # empty: NULL allowed
     assert decode(lib, o=P(FAKE[0].value + 2)) == ALIAS
 
 
@@ -139,6 +145,7 @@ def test_prefill_global_rope_validation(lib):
     assert call(Hq=15) == SHAPE
     assert call(k_rot=P(FAKE[1].value + 64)) == ALIAS   # k_rot over k
     assert call(k_rot=P(FAKE[4].value + 64)) == ALIAS   # k_rot over o
+    assert call(T=87382, Hq=64) == SHAPE               # q past 32-bit offsets
     assert call(B=0) == OK
 
 
