@@ -45,7 +45,9 @@
  *    2^31; the global prefills, windows over 129 and all fp32 prefills address
  *    one sequence's q with 32-bit byte offsets, so T*Hq*dqk*(element size) must
  *    stay below 2^31 (bf16, 64 query heads: T <= 87381); the sliding-window
- *    bf16 prefills (W <= 129) have no per-sequence limit.
+ *    bf16 prefills (W <= 129) have no per-sequence limit.  A cache's rows of
+ *    one (sequence, KV head) likewise: cap*dqk*(cache element size) below 2^31
+ *    (bf16: cap <= 5592405).
  *  - A call with nothing to do (B*T == 0 for a prefill or backward; B == 0 for
  *    decode, verify and advance_len; B*n == 0 for kv_append; n_tok == 0 for
  *    RoPE) returns SINKATTN_OK with no HIP call; its data pointers may be NULL.

@@ -139,8 +139,10 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
         return SINKATTN_ERR_SHAPE;
     if (dtype == SINKATTN_BF16 && nq * (Hq / Hkv) > 64)
         return SINKATTN_ERR_UNSUPPORTED;
+    // a (sequence, KV head)'s cache rows are addressed with 32-bit byte offsets
     if ((int64_t)max_len_hint + nq > INT_MAX / 2 || (int64_t)B * nq * Hq > INT_MAX ||
-        (int64_t)B * Hkv * cap > (int64_t)INT_MAX * 8)
+        (int64_t)B * Hkv * cap > (int64_t)INT_MAX * 8 ||
+        (int64_t)cap * kDqk * (fp8 ? 1 : (int64_t)esize(dtype)) > INT_MAX)
         return SINKATTN_ERR_SHAPE;
     if (kind == SINKATTN_CACHE_RING) {
         if (window < 1)

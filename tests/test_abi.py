@@ -101,6 +101,7 @@ def test_decode_validation(lib):
     assert decode(lib, max_len=-1) == SHAPE
     assert decode(lib, dtype=2) == DTYPE
     assert decode(lib, B=0) == OK
+    assert decode(lib, kind=1, cap=5592406) == SHAPE   # cache rows past 32-bit offsets
     assert decode(lib, B=0, q=None, cache_len=None, o=None) == OK   # empty: NULL allowed
     assert decode(lib, o=P(FAKE[0].value + 2)) == ALIAS
 
