@@ -119,19 +119,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     if (rlo >= rhi)
         return;  // uniform: this chunk holds no visible key
 
-    // RoPE (when fused): (cos, sin) of positions P .. P+nq-1 for q and the new keys.
-    if (a.rope) {
-        rope_fill_table64(rope_tab, P, nq, a.rope_base, tid, kThreads);
-        __syncthreads();
-    }
-    // The chunk holding position P stores the new token (decode) / rotated keys.
-    if (P >= rlo && P < rhi) {
-        if (a.rope)
-            cached_store_new<true, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
-        else
-            cached_store_new<false, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
-    }
-
     const uint64_t cache_rows = a.ring ? (uint64_t)a.cap : (uint64_t)P;
     const BufRsrc kc = make_buf((const uint8_t *)a.k_cache + crow0 * kDqk * kEs,
                                 cache_rows * kDqk * kEs);
@@ -143,36 +130,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
                                 ((uint64_t)(nq - 1) * Hkv + 1) * kDv * 2);
 
     // Q^T operand (B of the QK MFMA): column col = (token t, head) = divmod(col, group).
+    // Issued first, rotated once the RoPE table is ready.
     const int col = kTok ? kCols * wave + lr : lr;
     const bool col_ok = col < n_cols;
     const int qpos = col_ok ? P + col / group : -1;
-    bf16x8 qf[kDqk / 32];
+    uint4 qr[kDqk / 32];
     {
         const BufRsrc qb = make_buf((const uint16_t *)a.q + (size_t)b * nq * Hq * kDqk,
                                     (uint64_t)nq * Hq * kDqk * 2);
         const uint32_t off =
             col_ok ? (uint32_t)((col / group) * Hq + g * group + col % group) * kDqk * 2 : kOob;
-        uint4 qr[kDqk / 32];
 #pragma unroll
         for (int s = 0; s < kDqk / 32; ++s)
             qr[s] = buf_load16(qb, off + (uint32_t)kdim0<kFp8>(s, kg) * 2);
-        if (a.rope && col_ok) {  // k-steps 0, 1 hold dims < 64: 8-dim chunk kdim0/8
-            const float2 *cs = rope_tab + (col / group) * 32;
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                qr[s] = rope_chunk_bf16(qr[s], cs + 4 * (kdim0<kFp8>(s, kg) / 8));
-        }
-#pragma unroll
-        for (int s = 0; s < kDqk / 32; ++s)
-            qf[s] = as_bf16x8(qr[s]);
     }
-
-    float m = -INFINITY, l = 0.f;
-    f32x4v acc[8];
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-        acc[db] = f32x4v{};
-
     const int ce = min(rhi, P);
     const int n_cache_blk = ce > rlo ? (ce - rlo + kKb - 1) / kKb : 0;
     const int new_lo = max(rlo, P);
@@ -241,6 +212,52 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             x.v[e] = buf_load16(vn, off);
         }
     };
+    // The wave's first cache block is requested before the RoPE table and the
+    // new-token store, so its memory latency overlaps that work (the store
+    // writes position P, which no cache block reads).
+    KVc x;
+    if constexpr (kTok) {
+        if (kCols * wave < n_cols && n_cache_blk > 0) {
+            load_k(0, x);
+            load_v(0, x);
+        }
+    } else {
+        if (wave < n_cache_blk) {
+            load_k(wave, x);
+            load_v(wave, x);
+        }
+    }
+
+    // RoPE (when fused): (cos, sin) of positions P .. P+nq-1 for q and the new keys.
+    if (a.rope) {
+        rope_fill_table64(rope_tab, P, nq, a.rope_base, tid, kThreads);
+        __syncthreads();
+    }
+    // The chunk holding position P stores the new token (decode) / rotated keys.
+    if (P >= rlo && P < rhi) {
+        if (a.rope)
+            cached_store_new<true, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
+        else
+            cached_store_new<false, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
+    }
+
+    bf16x8 qf[kDqk / 32];
+    if (a.rope && col_ok) {  // k-steps 0, 1 hold dims < 64: 8-dim chunk kdim0/8
+        const float2 *cs = rope_tab + (col / group) * 32;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            qr[s] = rope_chunk_bf16(qr[s], cs + 4 * (kdim0<kFp8>(s, kg) / 8));
+    }
+#pragma unroll
+    for (int s = 0; s < kDqk / 32; ++s)
+        qf[s] = as_bf16x8(qr[s]);
+
+    float m = -INFINITY, l = 0.f;
+    f32x4v acc[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+        acc[db] = f32x4v{};
+
     // x is a cache block (KVc, prefetching the wave's next block jn) or the
     // new-token block (KV16 read from k_new / v_new, bf16 even with E4M3 caches).
     auto compute = [&](int j, int jn, auto &x) {
@@ -331,15 +348,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // per SIMD).
     if constexpr (kTok) {
         if (kCols * wave < n_cols) {  // wave-uniform: this wave owns some columns
-            {
-                KVc x;
-                if (n_cache_blk > 0) {
-                    load_k(0, x);
-                    load_v(0, x);
-                }
-                for (int j = 0; j < n_cache_blk; ++j)
-                    compute(j, j + 1, x);
-            }
+            for (int j = 0; j < n_cache_blk; ++j)
+                compute(j, j + 1, x);
             if (nblk > n_cache_blk) {
                 KV16 xn;
                 load_new(xn);
@@ -347,15 +357,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             }
         }
     } else {
-        {
-            KVc x;
-            if (wave < n_cache_blk) {
-                load_k(wave, x);
-                load_v(wave, x);
-            }
-            for (int j = wave; j < n_cache_blk; j += kWaves)
-                compute(j, j + kWaves, x);
-        }
+        for (int j = wave; j < n_cache_blk; j += kWaves)
+            compute(j, j + kWaves, x);
         if (nblk > n_cache_blk && n_cache_blk % kWaves == wave) {
             KV16 xn;
             load_new(xn);
