@@ -47,10 +47,12 @@ def parse():
                    help="untimed seconds of steps before the warm-up steps (clock ramp)")
     p.add_argument("--only", default="", help="comma list of: swa,global,decode,verify,spec,backward")
     p.add_argument("--counter-pass", nargs="?", const="swa", default=None,
-                   choices=["swa", "decode"],
+                   choices=["swa", "decode", "global"],
                    help="for rocprofv3 --pmc runs: one 1 GiB device copy (the calibration "
                         "kernel of known traffic), then 3 launches of the headline kernel "
-                        "(swa) or of the global layer of the hybrid decode step (decode)")
+                        "(swa), of the global layer of the hybrid decode step (decode), or "
+                        "of the fused global prefill followed by 3 bf16 8192^3 torch "
+                        "matmuls, a vendor GEMM to compare busy-cycle counters with (global)")
     return p.parse_args()
 
 
@@ -196,7 +198,7 @@ def run_swa_prefill(torch, ops, synth, steps, warmup, dev, prewarm_s=1.0, fused_
     return res, inputs
 
 
-def run_global_prefill(torch, ops, synth, dev, reps=5):
+def run_global_prefill(torch, ops, synth, dev, reps=5, counter_pass=False):
     w = synth.WORKLOADS[3]
     B, T, Hq, Hkv = w.B, w.T, w.Hq, w.Hkv
     q = synth.device_normal(w.seed, (B, T, Hq, 192), device=dev)
@@ -209,6 +211,17 @@ def run_global_prefill(torch, ops, synth, dev, reps=5):
     # the step: partial RoPE fused (k rotated once into k_rot, q on load)
     ft, kt, rt = Timer(torch), Timer(torch), Timer(torch)
     ops.prefill_global_rope(q, k, v, sink, w.base, k_rot=k_rot, out=o)  # warm-up
+    if counter_pass:  # 3 more launches of the fused kernel for rocprofv3 --pmc
+        for _ in range(3):
+            ops.prefill_global_rope(q, k, v, sink, w.base, k_rot=k_rot, out=o)
+        torch.cuda.synchronize()
+        del q, k, v, o, k_rot
+        a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+        b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        return None
     for _ in range(reps):
         with ft:
             ops.prefill_global_rope(q, k, v, sink, w.base, k_rot=k_rot, out=o)
@@ -696,6 +709,8 @@ def main():
         if args.counter_pass == "decode":
             r = run_hybrid_decode(torch, ops, synth, dev, counter_pass=True)
             log("[bench] global decode layer: %d KV bytes" % r["kv_bytes_global"])
+        elif args.counter_pass == "global":
+            run_global_prefill(torch, ops, synth, dev, counter_pass=True)
         else:
             run_swa_prefill(torch, ops, synth, steps=3, warmup=0, dev=dev, prewarm_s=0.0,
                             fused_only=True)
