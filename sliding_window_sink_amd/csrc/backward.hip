@@ -279,7 +279,7 @@ struct DkvSmem {
             uint16_t qr[kKWaves][kTq * kQRPitch];
             uint16_t gr[kKWaves][kTq * kGRPitch];
         } w;
-        float red[(kDqk + kDv) * kRedPitch];
+        float red[2][(kDqk + kDv) * kRedPitch];
     };
 };
 
@@ -433,32 +433,56 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a, int n_un
         }
     }
 
-    // Sum the 4 waves' partials in a fixed order through LDS, then write rows.
+    // Sum the 4 waves' partials in the fixed order (w0 + w2) + (w1 + w3) through two
+    // LDS regions: waves 0 and 1 store theirs, waves 2 and 3 then add theirs into
+    // region wave & 1 (every read of a lane issued before its writes, so the wave
+    // pays one LDS latency rather than one per element), and the row writer adds
+    // the two regions.
+    float *red = sm.red[wave & 1];
+    auto red_at = [&](int row) -> float & { return red[row * kRedPitch + r]; };
     __syncthreads();
-    for (int w = 0; w < kKWaves; ++w) {
-        if (wave == w) {
+    if (wave < 2) {
 #pragma unroll
-            for (int d = 0; d < kDqk / 32; ++d)
+        for (int d = 0; d < kDqk / 32; ++d)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float &x = sm.red[(32 * d + c_row(i, hh)) * kRedPitch + r];
-                    x = (w == 0 ? 0.f : x) + dk[d][i];
-                }
+            for (int i = 0; i < 16; ++i)
+                red_at(32 * d + c_row(i, hh)) = dk[d][i];
 #pragma unroll
-            for (int d = 0; d < kDv / 32; ++d)
+        for (int d = 0; d < kDv / 32; ++d)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float &x = sm.red[(kDqk + 32 * d + c_row(i, hh)) * kRedPitch + r];
-                    x = (w == 0 ? 0.f : x) + dv[d][i];
-                }
-        }
-        __syncthreads();
+            for (int i = 0; i < 16; ++i)
+                red_at(kDqk + 32 * d + c_row(i, hh)) = dv[d][i];
     }
+    __syncthreads();
+    if (wave >= 2) {
+        float pk[kDqk / 32][16], pv[kDv / 32][16];
+#pragma unroll
+        for (int d = 0; d < kDqk / 32; ++d)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                pk[d][i] = red_at(32 * d + c_row(i, hh));
+#pragma unroll
+        for (int d = 0; d < kDv / 32; ++d)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                pv[d][i] = red_at(kDqk + 32 * d + c_row(i, hh));
+#pragma unroll
+        for (int d = 0; d < kDqk / 32; ++d)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                red_at(32 * d + c_row(i, hh)) = pk[d][i] + dk[d][i];
+#pragma unroll
+        for (int d = 0; d < kDv / 32; ++d)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                red_at(kDqk + 32 * d + c_row(i, hh)) = pv[d][i] + dv[d][i];
+    }
+    __syncthreads();
     for (int idx = tid; idx < kKb * (kDqk + kDv); idx += kKThreads) {
         const int kk = idx / (kDqk + kDv), dim = idx % (kDqk + kDv);
         if (kb + kk >= T)
             continue;
-        const float x = sm.red[dim * kRedPitch + kk];
+        const float x = sm.red[0][dim * kRedPitch + kk] + sm.red[1][dim * kRedPitch + kk];
         const size_t trow = (row0 + kb + kk) * Hkv + g;
         if (dim < kDqk)
             a.dk[trow * kDqk + dim] = x * a.scale;
