@@ -39,9 +39,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
     return __builtin_bit_cast(float, (uint32_t)h << 16);
 }
-// Two floats -> one dword holding (lo, hi) bf16.
+// Two floats -> one dword holding (lo, hi) bf16, round to nearest even.  Built as
+// a two-element vector so the pair becomes one v_cvt_pk_bf16_f32 (packing two
+// separate conversions costs a shift and an or on top of two conversions).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    const bf16x2v v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

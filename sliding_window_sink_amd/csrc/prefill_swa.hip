@@ -274,11 +274,12 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
             // the test is uniform, so the mask sits behind a scalar branch
             const bool full = (kb + kKb - 1 <= t0) && (t0 + kTq - 1 - kb < window);
             if (!full) {
+                // key kb + 16hh + i is visible iff 0 <= query - key < window: one
+                // unsigned compare of d - i per element
+                const uint32_t d = (uint32_t)(query - kb - 16 * hh);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kb + 16 * hh + i;
-                    sc[i] = (key <= query && query - key < window) ? sc[i] : -INFINITY;
-                }
+                for (int i = 0; i < 16; ++i)
+                    sc[i] = (d - (uint32_t)i < (uint32_t)window) ? sc[i] : -INFINITY;
             }
             float bm = -INFINITY;
 #pragma unroll
