@@ -687,8 +687,8 @@ def cpu_baseline(torch, inputs, target_s: float):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs no multi-GPU path "
-              "(collectives/sharding are a design note); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only (no collective or sharded path is "
+              "implemented); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 
