@@ -48,6 +48,7 @@ constexpr int kVPitch = kKb + 8;    // 80-byte LDS rows for V^T
 constexpr int kKChunks = kKb * kDqk / 8;  // 768 16-byte pieces per key block
 constexpr int kVChunks = kKb * kDv / 8;   // 512
 constexpr int kPairs = 32;          // rope_dim / 2 with rope_dim = 64
+constexpr int kMaxWinBlocks = kSlots - 1;  // key blocks a tile's window spans (W <= 129)
 static_assert(kVChunks == kThreads, "one V piece per thread");
 
 struct SwaSmem {
@@ -58,6 +59,7 @@ struct SwaSmem {
     // entries), and by 32*floor(p/32) * theta_c for one block (double buffered)
     double2 lo_rot[kPairs][kTq];
     double2 hi_rot[2][kPairs];
+    double2 hi_pro[kMaxWinBlocks - 1][kPairs];  // the prologue's other window blocks
     double inv_freq[kPairs];
 };
 
@@ -127,11 +129,12 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
         if (tid < kPairs)
             sm.hi_rot[buf][tid] = rope_sincos64(t, sm.inv_freq[tid]);
     };
-    // (cos, sin) of pairs c0..c0+3 of the token at offset j of the block in hi_rot[buf]
-    auto rot4 = [&](int buf, int j, int c0, float2 (&cs)[4]) {
+    // (cos, sin) of pairs c0..c0+3 of the token at offset j of the block whose
+    // rotation by its base position is hi[]
+    auto rot4 = [&](const double2 *hi, int j, int c0, float2 (&cs)[4]) {
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            cs[p] = rope_compose(sm.hi_rot[buf][c0 + p], sm.lo_rot[c0 + p][j]);
+            cs[p] = rope_compose(hi[c0 + p], sm.lo_rot[c0 + p][j]);
     };
 
     // ---- key blocks: global -> registers -> (rotate) -> LDS ring slot ----
@@ -161,8 +164,9 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
             kreg[1] = buf_load16(kbuf, rel * krow + kg_off[1]);
         vreg = buf_load16(vbuf, rel * vrow + vg_off);
     };
-    // cs_buf: hi_rot buffer of the block's tokens (rope only); own: this run writes k_rot
-    auto store_block = [&](int jb, const uint4 (&kreg)[2], const uint4 &vreg, int cs_buf,
+    // hi: rotation table of the block's base position (rope only); own: this run
+    // writes k_rot
+    auto store_block = [&](int jb, const uint4 (&kreg)[2], const uint4 &vreg, const double2 *hi,
                            bool own) {
         const int slot = jb % kSlots;
         const uint32_t rel = (uint32_t)(jb * kKb - tbase);
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
                 uint4 x = kreg[u];
                 if (kRope && k_d[u] < 8) {
                     float2 cs[4];
-                    rot4(cs_buf, k_key[u], 4 * k_d[u], cs);
+                    rot4(hi, k_key[u], 4 * k_d[u], cs);
                     x = rope_chunk_bf16(x, cs);
                 }
                 *(uint4 *)&sm.k[slot][kl_off[u]] = x;
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
 #pragma unroll
             for (int s = 0; s < 4; ++s) {  // dims < 64: chunks 2s+hh < 8
                 float2 cs[4];
-                rot4(cs_buf, r, 4 * (2 * s + hh), cs);
+                rot4(sm.hi_rot[cs_buf], r, 4 * (2 * s + hh), cs);
                 qr[s] = rope_chunk_bf16(qr[s], cs);
             }
         }
@@ -209,21 +213,34 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
     // end of tile i-2, or here) and published by that tile's closing barrier.
     uint4 qcur[kDqk / 16];
     {
+        // All of the first tile's window blocks are requested at once (one memory
+        // latency rather than one per block), their rotation tables computed side
+        // by side: block jhi (the tile's own) in hi_rot[cb], the others in hi_pro.
         const int t0 = tile_begin * kTq;
         const int jlo = first_block(t0), jhi = t0 / kKb;
         const int cb = tile_begin & 1;
-        for (int jb = jlo; jb <= jhi; ++jb) {
-            uint4 kreg[2], vreg;
-            if (kRope) {
-                fill_hi(cb, jb * kKb);
-                __syncthreads();
-            }
-            load_block(jb, kreg, vreg);
-            store_block(jb, kreg, vreg, cb, jb == jhi);
-            __syncthreads();
-        }
+        const int nb = jhi - jlo + 1;  // 1 .. kMaxWinBlocks
+        uint4 kr[kMaxWinBlocks][2], vr[kMaxWinBlocks];
+#pragma unroll
+        for (int i = 0; i < kMaxWinBlocks; ++i)
+            if (i < nb)
+                load_block(jlo + i, kr[i], vr[i]);
         load_q(t0, qcur);
-        rotate_q(qcur, cb);  // hi_rot[cb] now holds block jhi = this tile
+        if (kRope && tid < kPairs * nb) {
+            const int i = tid / kPairs, c = tid % kPairs;
+            const double2 x = rope_sincos64((jlo + i) * kKb, sm.inv_freq[c]);
+            if (i == nb - 1)
+                sm.hi_rot[cb][c] = x;
+            else
+                sm.hi_pro[i][c] = x;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kMaxWinBlocks; ++i)
+            if (i < nb)
+                store_block(jlo + i, kr[i], vr[i], i == nb - 1 ? sm.hi_rot[cb] : sm.hi_pro[i],
+                            i == nb - 1);
+        rotate_q(qcur, cb);
         __syncthreads();
         if (kRope && tile_begin + 1 < tile_end)
             fill_hi(cb ^ 1, t0 + kTq);
@@ -323,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
         // wait on the prefetch can also end up waiting on the stores.
         if (has_next) {
             const int nb = (tile + 1) & 1;  // table of the next tile's tokens
-            store_block(jhi + 1, kreg, vreg, nb, true);
+            store_block(jhi + 1, kreg, vreg, sm.hi_rot[nb], true);
             rotate_q(qnext, nb);
         }
 
