@@ -61,6 +61,29 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(T *x, int64_t n_tok, int
     }
 }
 
+// The common case -- bf16 rows, interleaved pairs, rope_dim 64, head_dim a
+// multiple of 8, 16-byte aligned rows -- with 16-byte accesses: one thread per
+// 8-dim chunk of the rotated dims (four pairs), the same cos/sin and rounding as
+// rope_kernel.  (rope_kernel moves 2-byte elements, which leaves the memory
+// system mostly idle.)
+__global__ __launch_bounds__(kThreads) void rope_vec_kernel(uint16_t *x, int64_t n_tok, int n_heads,
+                                                            int head_dim, const int32_t *pos,
+                                                            double base) {
+    __shared__ float2 cs[kTokens * 32];
+    const int64_t tok0 = (int64_t)blockIdx.x * kTokens;
+    const int ntok = (int)min<int64_t>(kTokens, n_tok - tok0);
+    for (int idx = threadIdx.x; idx < ntok * 32; idx += kThreads)
+        cs[idx] = rope_cos_sin(pos[tok0 + (idx >> 5)], rope_inv_freq(base, idx & 31, 64));
+    __syncthreads();
+    const int per_tok = n_heads * 8;  // 8 chunks of 8 dims = the 64 rotated dims
+    for (int idx = threadIdx.x; idx < ntok * per_tok; idx += kThreads) {
+        const int tt = idx / per_tok, rem = idx % per_tok;
+        const int h = rem >> 3, ci = rem & 7;
+        uint4 *p = (uint4 *)(x + ((tok0 + tt) * n_heads + h) * (int64_t)head_dim) + ci;
+        *p = rope_chunk_bf16(*p, cs + tt * 32 + 4 * ci);
+    }
+}
+
 // Out-of-place variant for bf16 rows of 192 dims at positions 0..T-1 of each
 // sequence (the keys of a prefill with the RoPE fused): one thread per 16-byte
 // chunk; chunks 0..7 (dims 0..63, interleaved pairs) are rotated with the same
@@ -104,7 +127,11 @@ hipError_t launch_rope(void *x, int bf16, int64_t n_tok, int n_heads, int head_d
     if (n_tok == 0 || n_heads == 0 || rope_dim == 0)
         return hipSuccess;
     const unsigned blocks = (unsigned)((n_tok + kTokens - 1) / kTokens);
-    if (bf16)
+    if (bf16 && style == 0 && rope_dim == 64 && head_dim % 8 == 0 &&
+        reinterpret_cast<uintptr_t>(x) % 16 == 0)
+        rope_vec_kernel<<<dim3(blocks), dim3(kThreads), 0, s>>>((uint16_t *)x, n_tok, n_heads,
+                                                                head_dim, pos, base);
+    else if (bf16)
         rope_kernel<uint16_t><<<dim3(blocks), dim3(kThreads), 0, s>>>(
             (uint16_t *)x, n_tok, n_heads, head_dim, rope_dim, pos, base, style);
     else
