@@ -76,18 +76,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // dsink_h = sum over (b, t) of PS[b][h][t]: one workgroup per head, fixed order.
-__global__ __launch_bounds__(256) void bwd_dsink_kernel(BwdArgs a) {
-    __shared__ float red[256];
+constexpr int kSinkThreads = 1024;
+__global__ __launch_bounds__(kSinkThreads) void bwd_dsink_kernel(BwdArgs a) {
+    __shared__ float red[kSinkThreads];
     const int h = blockIdx.x;
     float s = 0.f;
     for (int b = 0; b < a.B; ++b) {
         const float *p = a.PS + ((size_t)b * a.Hq + h) * a.T;
-        for (int t = threadIdx.x; t < a.T; t += 256)
+        for (int t = threadIdx.x; t < a.T; t += kSinkThreads)
             s += p[t];
     }
     red[threadIdx.x] = s;
     __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
+    for (int w = kSinkThreads / 2; w >= 1; w >>= 1) {
         if ((int)threadIdx.x < w)
             red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
@@ -501,7 +502,7 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    bwd_dsink_kernel<<<dim3((unsigned)a.Hq), dim3(256), 0, s>>>(a);
+    bwd_dsink_kernel<<<dim3((unsigned)a.Hq), dim3(kSinkThreads), 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int group = a.Hq / a.Hkv;
