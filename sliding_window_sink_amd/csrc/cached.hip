@@ -425,12 +425,28 @@ __global__ __launch_bounds__(64) void combine_kernel(CachedArgs a, int out_bf16)
     float z = 0.f, acc0 = 0.f, acc1 = 0.f;
     if (mx != -INFINITY) {
         z = (sink2 == -INFINITY) ? 0.f : fast_exp2(sink2 - mx);
-        for (int s = s0; s < s1; ++s) {
-            const float ms = wm[s];
-            const float f = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mx);
-            z += wl[s] * f;
-            acc0 += wa[(size_t)s * kDv + lane] * f;
-            acc1 += wa[(size_t)s * kDv + 64 + lane] * f;
+        // Splits in groups of kGroup: all loads of a group are issued before
+        // any is used (indices past the last split repeat it and get weight
+        // 0), so a row waits for one memory latency per group, not per split.
+        constexpr int kGroup = 8;
+        for (int s = s0; s < s1; s += kGroup) {
+            float ms[kGroup], ls[kGroup], a0[kGroup], a1[kGroup];
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) {
+                const int sj = min(s + j, s1 - 1);
+                ms[j] = wm[sj];
+                ls[j] = wl[sj];
+                a0[j] = wa[(size_t)sj * kDv + lane];
+                a1[j] = wa[(size_t)sj * kDv + 64 + lane];
+            }
+#pragma unroll
+            for (int j = 0; j < kGroup; ++j) {
+                const float f =
+                    (s + j >= s1 || ms[j] == -INFINITY) ? 0.f : fast_exp2(ms[j] - mx);
+                z += ls[j] * f;
+                acc0 += a0[j] * f;
+                acc1 += a1[j] * f;
+            }
         }
     }
     const float inv = z > 0.f ? 1.f / z : 0.f;
