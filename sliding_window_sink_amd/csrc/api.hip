@@ -183,15 +183,18 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
             int64_t c = (span + num_splits - 1) / num_splits;
             chunk = (int)((c + 127) / 128 * 128);
         } else {
-            // automatic: ~24 workgroups per compute unit over the longest sequence,
-            // but chunks of at least 112 keys per (token, head) column, so that a
-            // workgroup's fixed costs (its q, the merge, 520 B of partial state per
-            // column) stay small next to the K/V bytes it streams (640 B per key):
-            // measured at batch 64 x 16K, verify of 4 tokens 0.74 -> 0.61 ms and
-            // decode 0.57 -> 0.54 ms against a floor of 28 keys per column.
+            // automatic: ~24 workgroups per compute unit over the longest sequence
+            // (sequences of unequal length need the finer pieces to even out the
+            // work per compute unit), but chunks of at least 176 keys per (token,
+            // head) column, so that a workgroup's fixed costs (its q, the merge,
+            // 520 B of partial state per column) stay small next to the K/V bytes
+            // it streams (640 B per key).  Measured at batch 64 x 16K: decode
+            // 0.527 -> 0.488 ms (10 -> 6 splits) against a floor of 112 keys per
+            // column; unchanged at batch 32 over 16K-128K contexts (47 splits of
+            // 2816 keys, where 24 or 12 longer splits ran 6-10% slower).
             const int64_t cus = device_cu_count();
             int64_t c = ((int64_t)B * Hkv * span + 24 * cus - 1) / (24 * cus);
-            c = std::max<int64_t>(c, 112 * (int64_t)n_cols);
+            c = std::max<int64_t>(c, 176 * (int64_t)n_cols);
             c = (c + 127) / 128 * 128;
             const int64_t want = (span + c - 1) / c;
             const int64_t room = workspace ? (int64_t)(ws_bytes / per_split) : 0;
