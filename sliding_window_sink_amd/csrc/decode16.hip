@@ -36,17 +36,6 @@
 namespace sinkattn {
 namespace {
 
-// Cache rows are read once per step: loads with the gfx950 "nt" (non-temporal)
-// cache policy, cache-policy operand bit 1 (about 1% faster on the long-context
-// global layer than the default policy; the "sc1" policy was 5% slower).
-constexpr int kCpolNt = 2;
-__device__ __forceinline__ uint4 buf_load16_stream(BufRsrc r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNt));
-}
-__device__ __forceinline__ uint2 buf_load8_stream(BufRsrc r, uint32_t off) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolNt));
-}
-
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
@@ -178,12 +167,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
                 const uint32_t off = p < ce ? (uint32_t)slot * kDqk + (uint32_t)kg * 16 : kOob;
 #pragma unroll
                 for (int u = 0; u < kDqk / 64; ++u)
-                    x.k[kt][u] = buf_load16_stream(kc, off + (uint32_t)u * 64);
+                    x.k[kt][u] = buf_load16(kc, off + (uint32_t)u * 64);
             } else {
                 const uint32_t off = p < ce ? (uint32_t)slot * kDqk * 2 : kOob;
 #pragma unroll
                 for (int s = 0; s < kDqk / 32; ++s)
-                    x.k[kt][s] = buf_load16_stream(kc, off + (uint32_t)kdim0<false>(s, kg) * 2);
+                    x.k[kt][s] = buf_load16(kc, off + (uint32_t)kdim0<false>(s, kg) * 2);
             }
         }
     };
@@ -196,9 +185,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             const uint32_t off =
                 p < ce ? ((uint32_t)slot * kDv + (uint32_t)lr * 8) * kEs : kOob;
             if constexpr (kFp8)
-                x.v[e] = buf_load8_stream(vc, off);
+                x.v[e] = buf_load8(vc, off);
             else
-                x.v[e] = buf_load16_stream(vc, off);
+                x.v[e] = buf_load16(vc, off);
         }
     };
     auto load_new = [&](KV16 &x) {
