@@ -263,6 +263,21 @@ def test_decode_ring(dtype, Hq, Hkv):
         assert torch.equal(vc[b, :, L % 128], layer.v_new[b, 0])
 
 
+def test_decode_ring_wide_window():
+    """W = 512 (the width of the report's window-size ablation, Table 2) as a runtime
+    parameter of the ring decode: 513 visible keys over 17 key blocks."""
+    _print_case("decode ring W512")
+    lens = [0, 1, 300, 511, 512, 513, 3000]
+    cl = torch.tensor(lens, dtype=torch.int32)
+    layer = _layer(22, cl, 1, 16, 2, 512, torch.bfloat16)
+    o, kc, vc = _run_cached(layer, cl, ops.RING, 512, 512, 2, verify=False)
+    assert_close(o, _ref_cached(layer, cl, 512), torch.bfloat16, "ring decode W512")
+    kc, vc = kc.cpu(), vc.cpu()
+    for b, L in enumerate(lens):
+        assert torch.equal(kc[b, :, L % 512], layer.k_new[b, 0])
+        assert torch.equal(vc[b, :, L % 512], layer.v_new[b, 0])
+
+
 @pytest.mark.parametrize("splits,ws", [(1, 0), (2, 2), (7, 7), (0, 64), (0, 0)])
 def test_decode_contig_splits(splits, ws):
     """Global decode with the sink tuned to ~50% mass, several split counts:
