@@ -329,6 +329,17 @@ def test_verify_ring(dtype):
                        kc0.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
 
 
+def test_verify_ring_wide_window():
+    """4-token verify over a W = 512 ring (token-wave mode, up to 516 keys per query)."""
+    _print_case("verify ring W512")
+    cl = torch.tensor([0, 2, 509, 510, 512, 700, 4096], dtype=torch.int32)
+    layer = _layer(62, cl, 4, 64, 8, 512, torch.bfloat16)
+    kc0, vc0 = synth.fill_ring(layer, cl, 512, 8)
+    o, kc, vc = _run_cached(layer, cl, ops.RING, 512, 512, 8, verify=True)
+    assert_close(o, _ref_cached(layer, cl, 512), torch.bfloat16, "ring verify W512")
+    assert torch.equal(kc.cpu().view(torch.int16), kc0.view(torch.int16))
+
+
 @pytest.mark.parametrize("splits,ws", [(1, 0), (0, 64), (5, 5)])
 def test_verify_contig(splits, ws):
     _print_case("verify contig", splits, ws)
