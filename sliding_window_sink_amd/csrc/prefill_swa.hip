@@ -323,6 +323,10 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
                 for (int db = 0; db < 4; ++db)
                     acc[db] *= alpha;
             }
+            // Raised wave priority while issuing the PV products, so the SIMD's
+            // other wave (in its softmax) does not delay their issue: 0.5-2%
+            // faster (the same around the score products gave nothing).
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -334,6 +338,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
                 if (db & 1)
                     __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
 
         // The prefetched key block and Q are consumed before O is stored, so no
