@@ -160,7 +160,17 @@ def rope_partial(x: torch.Tensor, pos: torch.Tensor, base: float, rope_dim: int 
     return x
 
 
-def _prefill(fn_name, q, k, v, sink, window, scale, out, return_lse):
+def _lse_buffer(lse_out, B, Hq, T, device, return_lse):
+    """The caller's lse tensor [B,Hq,T] fp32 (lse_out), a new one, or None."""
+    if lse_out is not None:
+        _dev(lse_out)
+        if lse_out.shape != (B, Hq, T) or lse_out.dtype != torch.float32:
+            raise SinkAttnError(-2, "lse_out must be float32 [B,Hq,T]")
+        return lse_out
+    return torch.empty((B, Hq, T), dtype=torch.float32, device=device) if return_lse else None
+
+
+def _prefill(fn_name, q, k, v, sink, window, scale, out, return_lse, lse_out=None):
     _dev(q, k, v, sink, out)
     B, T, Hq, dqk = q.shape
     Hkv, dv = k.shape[2], v.shape[3]
@@ -171,7 +181,7 @@ def _prefill(fn_name, q, k, v, sink, window, scale, out, return_lse):
     o = out if out is not None else torch.empty((B, T, Hq, dv), dtype=q.dtype, device=q.device)
     if o.shape != (B, T, Hq, dv) or o.dtype != q.dtype:
         raise SinkAttnError(-2, "bad output tensor")
-    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    lse = _lse_buffer(lse_out, B, Hq, T, q.device, return_lse)
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o), _ptr(lse), B, T, Hq, Hkv, dqk, dv]
     if fn_name == "sinkattn_prefill_swa":
         args.append(int(window))
@@ -180,15 +190,19 @@ def _prefill(fn_name, q, k, v, sink, window, scale, out, return_lse):
     return (o, lse) if return_lse else o
 
 
-def prefill_swa(q, k, v, sink, window: int = 128, scale=None, out=None, return_lse=False):
-    """Causal sliding-window prefill: q [B,T,Hq,192], k [B,T,Hkv,192], v [B,T,Hkv,128]."""
-    return _prefill("sinkattn_prefill_swa", q, k, v, sink, window, scale, out, return_lse)
+def prefill_swa(q, k, v, sink, window: int = 128, scale=None, out=None, return_lse=False,
+                lse_out=None):
+    """Causal sliding-window prefill: q [B,T,Hq,192], k [B,T,Hkv,192], v [B,T,Hkv,128].
+    lse_out: optional caller-owned fp32 [B,Hq,T] that receives lse (implies return_lse)."""
+    return _prefill("sinkattn_prefill_swa", q, k, v, sink, window, scale, out,
+                    return_lse or lse_out is not None, lse_out)
 
 
 def prefill_swa_rope(q, k, v, sink, window: int = 128, base: float = 1e4, rope_dim: int = 64,
-                     k_rot=None, scale=None, out=None, return_lse=False):
+                     k_rot=None, scale=None, out=None, return_lse=False, lse_out=None):
     """SWA prefill with partial RoPE fused into the loads (q, k un-rotated and
     left untouched); k_rot, if given, receives the rotated k."""
+    return_lse = return_lse or lse_out is not None
     _dev(q, k, v, sink, out, k_rot)
     B, T, Hq, dqk = q.shape
     Hkv, dv = k.shape[2], v.shape[3]
@@ -197,7 +211,7 @@ def prefill_swa_rope(q, k, v, sink, window: int = 128, base: float = 1e4, rope_d
     if k_rot is not None and (k_rot.shape != k.shape or k_rot.dtype != k.dtype):
         raise SinkAttnError(-2, "k_rot must match k")
     o = out if out is not None else torch.empty((B, T, Hq, dv), dtype=q.dtype, device=q.device)
-    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    lse = _lse_buffer(lse_out, B, Hq, T, q.device, return_lse)
     _check(lib().sinkattn_prefill_swa_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o), _ptr(lse),
                                            _ptr(k_rot), B, T, Hq, Hkv, dqk, dv, int(window),
                                            _scale(scale), int(rope_dim), float(base),
@@ -205,13 +219,14 @@ def prefill_swa_rope(q, k, v, sink, window: int = 128, base: float = 1e4, rope_d
     return (o, lse) if return_lse else o
 
 
-def prefill_global(q, k, v, sink, scale=None, out=None, return_lse=False):
+def prefill_global(q, k, v, sink, scale=None, out=None, return_lse=False, lse_out=None):
     """Causal full-context prefill (global-attention layer)."""
-    return _prefill("sinkattn_prefill_global", q, k, v, sink, 0, scale, out, return_lse)
+    return _prefill("sinkattn_prefill_global", q, k, v, sink, 0, scale, out,
+                    return_lse or lse_out is not None, lse_out)
 
 
 def prefill_global_rope(q, k, v, sink, base: float = 5e6, rope_dim: int = 64, k_rot=None,
-                        scale=None, out=None, return_lse=False):
+                        scale=None, out=None, return_lse=False, lse_out=None):
     """Global prefill with partial RoPE fused (q, k un-rotated and left untouched).
     The rotated keys are written to k_rot (allocated here when not given), which
     is returned as the second element: (o, k_rot) or (o, lse, k_rot)."""
@@ -225,7 +240,8 @@ def prefill_global_rope(q, k, v, sink, base: float = 5e6, rope_dim: int = 64, k_
     if k_rot.shape != k.shape or k_rot.dtype != k.dtype:
         raise SinkAttnError(-2, "k_rot must match k")
     o = out if out is not None else torch.empty((B, T, Hq, dv), dtype=q.dtype, device=q.device)
-    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if return_lse else None
+    return_lse = return_lse or lse_out is not None
+    lse = _lse_buffer(lse_out, B, Hq, T, q.device, return_lse)
     _check(lib().sinkattn_prefill_global_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o),
                                               _ptr(lse), _ptr(k_rot), B, T, Hq, Hkv, dqk, dv,
                                               _scale(scale), int(rope_dim), float(base),
