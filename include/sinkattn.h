@@ -212,6 +212,34 @@ int sinkattn_decode(const void *q, const void *k_new, const void *v_new, void *k
                     void *workspace, size_t ws_bytes, int dtype, void *stream);
 
 /*
+ * sinkattn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments and results as sinkattn_decode, bit for bit, except that the
+ * split-K scratch is not passed in: it is a fixed array of
+ * SINKATTN_STATIC_SCRATCH_BYTES bytes of device memory inside the library,
+ * which every GPU the library runs on holds from the library's load until the
+ * process ends.  The call allocates nothing (no hipMalloc, no library
+ * allocator).  The first call on a device looks the array's address up once
+ * (hipGetSymbolAddress) and keeps it for that device.
+ *   num_splits: 0 = automatic, limited to what the scratch holds (each split
+ *   takes B * Hq * (dv + 2) * 4 bytes); an explicit S > 1 whose
+ *   sinkattn_decode_workspace_bytes(B, Hq, dv, 1, S) exceeds the scratch is
+ *   rejected with SINKATTN_ERR_WORKSPACE before anything is enqueued.
+ *   Nothing in the scratch has to start at zero: every split that the combine
+ *   step reads is written by the same call first.
+ *   All calls on one GPU share that GPU's scratch, so calls that overlap in
+ *   time on one GPU (different streams, or host threads on one stream without
+ *   ordering) race; calls ordered on one stream do not.
+ */
+#define SINKATTN_STATIC_SCRATCH_BYTES (32u << 20)
+
+int sinkattn_decode_noalloc(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                            void *v_cache, int kind, int cap, const int32_t *cache_len,
+                            int max_len_hint, const float *sink, void *o, int B, int Hq,
+                            int Hkv, int dqk, int dv, int window, float scale, int num_splits,
+                            int dtype, void *stream);
+
+/*
  * Multi-query speculative verification (Section 2.3.1 and Section 5: the main
  * model scores 1 + K draft tokens in one pass; Table 10 uses 3 draft heads).
  *   q [B,nq,Hq,dqk]; k_new/v_new [B,nq,Hkv,d]; o [B,nq,Hq,dv]; 1 <= nq <= 8.

@@ -4,7 +4,8 @@
 // SINKATTN_ERR_* code before touching the HIP runtime; only then does it
 // enqueue kernels on the caller's stream.  No device memory is allocated or
 // freed here; the only global state is the per-device compute-unit count used
-// by the split-K heuristic.
+// by the split-K heuristic and the per-device address of the fixed scratch
+// array of sinkattn_decode_noalloc.
 #include <algorithm>
 #include <climits>
 #include <cmath>
@@ -31,6 +32,36 @@ int device_cu_count() {
         cached[dev] = n;
     }
     return cached[dev];
+}
+
+// Split-K scratch of sinkattn_decode_noalloc: a fixed device array, so that
+// entry point allocates nothing.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address (one copy per GPU) is looked
+// up once per device with hipGetSymbolAddress and only that address is used.
+static __device__ __align__(256) unsigned char scratch[SINKATTN_STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch_address(void **out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (p == nullptr)
+            return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace sinkattn
@@ -113,7 +144,13 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
                   int window, float scale, int num_splits, void *workspace, size_t ws_bytes,
                   int dtype, void *stream, int write_new, int rope = 0, int rope_dim = 0,
                   double rope_base = 0.0, void *k_rot = nullptr, int fp8 = 0,
-                  float k_scale = 1.f, float v_scale = 1.f) {
+                  float k_scale = 1.f, float v_scale = 1.f, bool static_ws = false) {
+    // static_ws: the split-K scratch is the library's fixed device array; its
+    // address is looked up only after validation, when a split is taken
+    if (static_ws) {
+        workspace = nullptr;
+        ws_bytes = SINKATTN_STATIC_SCRATCH_BYTES;
+    }
     int st = check_heads(Hq, Hkv, dqk, dv, dtype);
     if (st)
         return st;
@@ -177,8 +214,9 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
     if (kind == SINKATTN_CACHE_CONTIG && dtype == SINKATTN_BF16 && num_splits != 1 && B > 0) {
         const int n_cols = nq * (Hq / Hkv);
         const size_t per_split = ws_bytes_for(B, Hq, dv, nq, 2) / 2;
+        const bool have_ws = workspace != nullptr || static_ws;
         if (num_splits > 1) {
-            if (!workspace || ws_bytes < per_split * (size_t)num_splits)
+            if (!have_ws || ws_bytes < per_split * (size_t)num_splits)
                 return SINKATTN_ERR_WORKSPACE;
             int64_t c = (span + num_splits - 1) / num_splits;
             chunk = (int)((c + 127) / 128 * 128);
@@ -197,7 +235,7 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
             c = std::max<int64_t>(c, 176 * (int64_t)n_cols);
             c = (c + 127) / 128 * 128;
             const int64_t want = (span + c - 1) / c;
-            const int64_t room = workspace ? (int64_t)(ws_bytes / per_split) : 0;
+            const int64_t room = have_ws ? (int64_t)(ws_bytes / per_split) : 0;
             const int64_t s_eff = std::min<int64_t>(want, room);
             if (s_eff >= 2) {
                 c = (span + s_eff - 1) / s_eff;
@@ -224,6 +262,10 @@ int cached_common(const void *q, const void *k_new, const void *v_new, void *k_c
     }
     if (B == 0)
         return SINKATTN_OK;
+    if (static_ws && splits > 1) {
+        if (hipError_t e = static_scratch_address(&workspace); e != hipSuccess)
+            return SINKATTN_ERR_HIP;
+    }
 
     CachedArgs a{};
     a.q = q;
@@ -460,6 +502,16 @@ int sinkattn_decode(const void *q, const void *k_new, const void *v_new, void *k
     return cached_common(q, k_new, v_new, k_cache, v_cache, kind, cap, cache_len, max_len_hint,
                          sink, o, B, 1, Hq, Hkv, dqk, dv, window, scale, num_splits, workspace,
                          ws_bytes, dtype, stream, 1);
+}
+
+int sinkattn_decode_noalloc(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                            void *v_cache, int kind, int cap, const int32_t *cache_len,
+                            int max_len_hint, const float *sink, void *o, int B, int Hq,
+                            int Hkv, int dqk, int dv, int window, float scale, int num_splits,
+                            int dtype, void *stream) {
+    return cached_common(q, k_new, v_new, k_cache, v_cache, kind, cap, cache_len, max_len_hint,
+                         sink, o, B, 1, Hq, Hkv, dqk, dv, window, scale, num_splits, nullptr, 0,
+                         dtype, stream, 1, 0, 0, 0.0, nullptr, 0, 1.f, 1.f, true);
 }
 
 int sinkattn_verify(const void *q, const void *k_new, const void *v_new, const void *k_cache,

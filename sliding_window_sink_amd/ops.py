@@ -57,6 +57,8 @@ def _bind(lib):
         "sinkattn_decode_workspace_bytes": ([i32, i32, i32, i32, i32], sz),
         "sinkattn_decode": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32, i32,
                              f32, i32, p, sz, i32, p], i32),
+        "sinkattn_decode_noalloc": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32,
+                                     i32, i32, f32, i32, i32, p], i32),
         "sinkattn_verify": ([p, p, p, p, p, i32, i32, p, i32, p, p, i32, i32, i32, i32, i32, i32,
                              i32, f32, i32, p, sz, i32, p], i32),
         "sinkattn_kv_append": ([p, p, p, p, i32, i32, p, p, i32, i32, i32, i32, i32, i32, p], i32),
@@ -103,7 +105,8 @@ EXPORTED = ["sinkattn_abi_version", "sinkattn_status_string", "sinkattn_rope_par
             "sinkattn_decode", "sinkattn_verify", "sinkattn_kv_append",
             "sinkattn_prefill_global_rope", "sinkattn_decode_rope", "sinkattn_verify_rope",
             "sinkattn_advance_len", "sinkattn_decode_fp8", "sinkattn_verify_fp8",
-            "sinkattn_kv_append_fp8", "sinkattn_backward_workspace_bytes", "sinkattn_backward"]
+            "sinkattn_kv_append_fp8", "sinkattn_backward_workspace_bytes", "sinkattn_backward",
+            "sinkattn_decode_noalloc"]
 
 
 def _check(rc: int):
@@ -303,6 +306,34 @@ def decode(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind=RING, window
         raise SinkAttnError(-2, "max_len_hint (host bound on cache_len) is required")
     return _cached(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind, window, max_len_hint,
                    num_splits, workspace, scale, out, verify=False)
+
+
+def decode_noalloc(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind=RING, window=128,
+                   max_len_hint=None, num_splits=0, scale=None, out=None):
+    """decode() whose split-K scratch is the library's fixed device array: the C
+    call allocates nothing (pass `out` to keep the whole call allocation-free)."""
+    if max_len_hint is None:
+        raise SinkAttnError(-2, "max_len_hint (host bound on cache_len) is required")
+    _dev(q, k_new, v_new, k_cache, v_cache, cache_len, sink, out)
+    if cache_len.dtype != torch.int32:
+        raise SinkAttnError(-3, "cache_len must be int32")
+    B, Hq, dqk = q.shape
+    Bc, Hkv, cap, dk = k_cache.shape
+    dv = v_cache.shape[3]
+    if Bc != B or dk != dqk or v_cache.shape[:3] != (B, Hkv, cap) or sink.shape != (Hq,):
+        raise SinkAttnError(-2, "cache / query shapes disagree")
+    if tuple(k_new.shape[:-1]) != (B, Hkv) or tuple(v_new.shape[:-1]) != (B, Hkv):
+        raise SinkAttnError(-2, "k_new/v_new shapes disagree")
+    o = out if out is not None else torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
+    _check(lib().sinkattn_decode_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                         _ptr(v_cache), int(kind), cap, _ptr(cache_len),
+                                         int(max_len_hint), _ptr(sink), _ptr(o), B, Hq, Hkv,
+                                         dqk, dv, int(window), _scale(scale), int(num_splits),
+                                         _dtype_code(q), _stream()))
+    return o
+
+
+STATIC_SCRATCH_BYTES = 32 << 20  # SINKATTN_STATIC_SCRATCH_BYTES of include/sinkattn.h
 
 
 def verify(q, k_new, v_new, k_cache, v_cache, cache_len, sink, kind=RING, window=128,

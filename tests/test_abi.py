@@ -30,7 +30,7 @@ def declared_symbols():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(ops.EXPORTED) == names
@@ -104,6 +104,29 @@ def test_decode_validation(lib):
     assert decode(lib, kind=1, cap=5592406) == SHAPE   # cache rows past 32-bit offsets
     assert decode(lib, B=0, q=None, cache_len=None, o=None) == OK   # empty: NULL allowed
     assert decode(lib, o=P(FAKE[0].value + 2)) == ALIAS
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode validates like sinkattn_decode, and rejects an
+    explicit split count whose scratch exceeds the fixed array (only cases that
+    fail before any HIP call are run here)."""
+    def dn(*, kind=1, cap=200000, max_len=131072, B=64, Hq=64, Hkv=4, window=0, splits=0,
+           dtype=1, q=FAKE[0], cache_len=FAKE[5], o=FAKE[9]):
+        return lib.sinkattn_decode_noalloc(q, FAKE[1], FAKE[2], FAKE[3], P(13 << 36), kind, cap,
+                                           cache_len, max_len, FAKE[6], o, B, Hq, Hkv, 192, 128,
+                                           window, 0.0, splits, dtype, None)
+    per_split = lib.sinkattn_decode_workspace_bytes(64, 64, 128, 1, 2) // 2
+    too_many = (32 << 20) // per_split + 1
+    assert dn(splits=too_many) == WS
+    assert dn(q=None) == NULL
+    assert dn(cache_len=None) == NULL
+    assert dn(kind=7) == UNSUP
+    assert dn(kind=0, cap=64, window=128) == CAP
+    assert dn(max_len=200000) == CAP
+    assert dn(dtype=3) == DTYPE
+    assert dn(Hq=62) == SHAPE
+    assert dn(B=0) == OK
+    assert dn(o=P(FAKE[0].value + 2)) == ALIAS
 
 
 def test_verify_validation(lib):
