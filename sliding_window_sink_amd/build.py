@@ -18,6 +18,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsinkattn.so")
+# calibration kernels of the benchmark's measured ceilings (not the attention path)
+CALIB_SRC = os.path.join(HERE, "calib", "stream_read.hip")
+CALIB_LIB = os.path.join(HERE, "libsinkattn_calib.so")
 ARCH = os.environ.get("SINKATTN_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -39,19 +42,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
-        objs = list(ex.map(_compile, sources))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources) + 1)) as ex:
+        calib = ex.submit(_compile, CALIB_SRC)
+        objs = list(ex.map(_compile, sources))
+        calib_obj = calib.result()
+    _link(objs, LIB)
+    _link([calib_obj], CALIB_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", CALIB_LIB)
     return LIB
 
 
