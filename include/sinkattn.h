@@ -200,7 +200,7 @@ size_t sinkattn_decode_workspace_bytes(int B, int Hq, int dv, int n_q, int max_s
  *   max_len_hint: host bound on max(cache_len); sizes the split grid.
  *   num_splits: CONTIG only: 0 = choose automatically, 1 = no split, S > 1 = at
  *          most S context chunks merged by an exact log-sum-exp combine that
- *          adds the sink once.  RING ignores it (<= W+1 keys).
+ *          adds the sink once.  RING ignores it (at most W keys).
  *   workspace / ws_bytes: fp32 scratch of sinkattn_decode_workspace_bytes(B,
  *          Hq, dv, 1, S) bytes for the chosen S > 1 (may be NULL when no split
  *          is taken; the automatic choice never exceeds what ws_bytes holds).
@@ -286,7 +286,9 @@ int sinkattn_verify_rope(const void *q, const void *k_new, const void *v_new,
                          void *stream);
 
 /*
- * Commit accepted tokens into a cache (the step after verification).
+ * Commit accepted tokens into a cache (Section 2.3.1: the main model verifies
+ * the draft tokens in one pass and the accepted ones join the context; this is
+ * the step after verification that stores them).
  *   k_new [B,n,Hkv,dqk], v_new [B,n,Hkv,dv]: tokens at positions
  *   cache_len[b] .. cache_len[b]+n-1.  n_accept: device int32 [B] (NULL = n):
  *   only tokens t < min(n_accept[b], n) are written.  RING: position p goes to

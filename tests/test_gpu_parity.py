@@ -265,7 +265,8 @@ def test_decode_ring(dtype, Hq, Hkv):
 
 def test_decode_ring_wide_window():
     """W = 512 (the width of the report's window-size ablation, Table 2) as a runtime
-    parameter of the ring decode: 513 visible keys over 17 key blocks."""
+    parameter of the ring decode: up to 512 visible keys (the query included) over
+    16 key blocks plus the new token."""
     _print_case("decode ring W512")
     lens = [0, 1, 300, 511, 512, 513, 3000]
     cl = torch.tensor(lens, dtype=torch.int32)
