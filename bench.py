@@ -55,12 +55,14 @@ def parse():
                    help="untimed seconds of steps before the warm-up steps (clock ramp)")
     p.add_argument("--only", default="", help="comma list of: swa,global,decode,verify,spec,backward")
     p.add_argument("--counter-pass", nargs="?", const="swa", default=None,
-                   choices=["swa", "decode", "global"],
+                   choices=["swa", "decode", "global", "ring", "verify"],
                    help="for rocprofv3 --pmc runs: one 1 GiB device copy (the calibration "
                         "kernel of known traffic), then 3 launches of the headline kernel "
                         "(swa), of the global layer of the hybrid decode step (decode), or "
                         "of the fused global prefill followed by 3 bf16 8192^3 torch "
-                        "matmuls, a vendor GEMM to compare busy-cycle counters with (global)")
+                        "matmuls, a vendor GEMM to compare busy-cycle counters with (global), "
+                        "of the first ring layer of the hybrid decode step (ring), or of the "
+                        "SWA and global verify layers, alternately (verify)")
     return p.parse_args()
 
 
@@ -523,6 +525,11 @@ def run_hybrid_decode(torch, ops, synth, dev, fp8=False, counter_pass=False):
             swa(r)
         glob()
 
+    if counter_pass == "ring":  # 3 eager launches of ring layer 0 for rocprofv3 --pmc
+        for _ in range(3):
+            swa(rings[0])
+        torch.cuda.synchronize()
+        return dict(kv_bytes_ring=B * 8 * 128 * 640)
     if counter_pass:  # 3 eager launches of the global layer for rocprofv3 --pmc
         for _ in range(3):
             glob()
@@ -569,7 +576,7 @@ def run_hybrid_decode(torch, ops, synth, dev, fp8=False, counter_pass=False):
                 global_tflops=gflops / glob_ms / 1e9, mean_ctx=float(cl.double().mean()))
 
 
-def run_verify(torch, ops, synth, dev):
+def run_verify(torch, ops, synth, dev, counter_pass=False):
     w = synth.WORKLOADS[5]
     B, nq, Hq, L = w.B, w.T, 64, 16384
     cap = L + 8
@@ -622,6 +629,12 @@ def run_verify(torch, ops, synth, dev):
         v_swa()
         v_glob()
 
+    if counter_pass:  # 3 eager launches of each verify layer for rocprofv3 --pmc
+        for _ in range(3):
+            v_swa()
+            v_glob()
+        torch.cuda.synchronize()
+        return None
     # cold graph replays (512 MB flush before each, outside the event pair), as
     # for the decode step; the SWA layer's own time from a graph of 5 such layers
     # over separate caches (divided by 5), so that launch gaps do not dominate it
@@ -860,6 +873,11 @@ def main():
         if args.counter_pass == "decode":
             r = run_hybrid_decode(torch, ops, synth, dev, counter_pass=True)
             log("[bench] global decode layer: %d KV bytes" % r["kv_bytes_global"])
+        elif args.counter_pass == "ring":
+            r = run_hybrid_decode(torch, ops, synth, dev, counter_pass="ring")
+            log("[bench] ring decode layer: %d KV bytes" % r["kv_bytes_ring"])
+        elif args.counter_pass == "verify":
+            run_verify(torch, ops, synth, dev, counter_pass=True)
         elif args.counter_pass == "global":
             run_global_prefill(torch, ops, synth, dev, counter_pass=True)
         else:
