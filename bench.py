@@ -10,8 +10,9 @@ and k [1,32768,8,192], then causal sink attention with W = 128 over v
 heads x 640 FLOP) per step divided by the step time.
 
 Timing protocol: every timed step (and every rep of the other workloads) is
-preceded by a 512 MB write that evicts L2 and the 256 MB Infinity Cache; the
-flush runs outside the step's HIP event pair, and the step time is the median
+preceded by a 512 MB write and a 512 MB read that evict L2 and the 256 MB
+Infinity Cache (leaving clean lines, so no write-back lands in the next step);
+the flush runs outside the step's HIP event pair, and the step time is the median
 of the K flushed steps (min and mean reported beside it, and the back-to-back
 rate for reference).  The decode and verify steps are HIP graphs replayed the
 same way (cold); their back-to-back replay is reported as the warm figure.
