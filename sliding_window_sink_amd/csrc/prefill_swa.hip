@@ -16,7 +16,11 @@
 //     tile (a 32-token tile sees 159 keys);
 //   - while tile i is computed, the next tile's Q (into registers) and its new
 //     key block (into registers, then into the free ring slot) are in flight;
-//   - one barrier per tile publishes the new key block.
+//   - one barrier per tile publishes the new key block;
+//   - with RoPE, the fp32 (cos, sin) of a tile's 32 tokens are composed once per
+//     tile into an LDS table (two entries per thread) that the Q of all 8 heads
+//     and the tile's key block read, instead of each wave composing them in
+//     fp64 for its own head.
 // All global traffic goes through raw buffer descriptors (a wave-uniform base
 // for the run plus a 32-bit lane offset): rows past the end of the sequence
 // read as zero and their stores are dropped by the hardware, so there are no
@@ -51,15 +55,18 @@ constexpr int kPairs = 32;          // rope_dim / 2 with rope_dim = 64
 constexpr int kMaxWinBlocks = kSlots - 1;  // key blocks a tile's window spans (W <= 129)
 static_assert(kVChunks == kThreads, "one V piece per thread");
 
+// RoPE.  A position splits as p = 32*floor(p/32) + (p mod 32); its (cos, sin)
+// is the fp64 composition of the rotations by the two parts, rounded to fp32
+// (rope_compose).  Tiles and key blocks are both 32 tokens, so one table of
+// fp32 (cos, sin) per tile serves the tile's Q (all 8 heads) and its key block.
 struct SwaSmem {
     uint16_t k[kSlots][kKb * kKPitch];
     uint16_t vt[kSlots][kDv * kVPitch];
-    // RoPE: rotation by (p mod 32) * theta_c for the 32 offsets (built once; pair
-    // major, so the 32 lanes of a wave -- one token each -- read consecutive
-    // entries), and by 32*floor(p/32) * theta_c for one block (double buffered)
-    double2 lo_rot[kPairs][kTq];
-    double2 hi_rot[2][kPairs];
-    double2 hi_pro[kMaxWinBlocks - 1][kPairs];  // the prologue's other window blocks
+    // tables of tiles t (buffer t & 1), pair major, so the 32 lanes of a wave --
+    // one token each -- read consecutive entries
+    float2 cs[2][kPairs][kTq];
+    double2 hi_rot[2][kPairs];                 // by the bases of tiles (buffer t & 1)
+    double2 hi_pro[kMaxWinBlocks][kPairs];     // by the bases of the prologue's blocks
     double inv_freq[kPairs];
 };
 
@@ -67,6 +74,13 @@ struct SwaRope {
     double base;
     uint16_t *k_rot;  // optional copy of rotated k [B,T,Hkv,192]
 };
+
+// rope_sincos64 as a real call, for the refill inside the tile loop: inlined,
+// the compiler keeps the fp64 sincos's polynomial constants in VGPR pairs
+// across the whole loop (16 registers the score loop can use instead).
+__device__ __attribute__((noinline)) double2 rope_sincos64_call(int p, double inv_freq) {
+    return rope_sincos64(p, inv_freq);
+}
 
 // V^T LDS row holding output dim d.  Block db, C-row rho = 8a + 4hh + e of the PV
 // accumulators holds dim 32a + 16(db/2) + 8hh + 4(db%2) + e, so for each (a, db/2)
@@ -117,24 +131,38 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
     const uint32_t qcol = (uint32_t)h * kDqk * 2, kcol = (uint32_t)g * kDqk * 2,
                    vcol = (uint32_t)g * kDv * 2, ocol = (uint32_t)h * kDv * 2;
 
+    // Each thread builds table entries (pair c_lo, token j) and (c_lo + 16, j) of
+    // every tile; it keeps the rotations of those two entries by j * theta_c in
+    // registers for the whole run.
+    const int c_lo = tid / kTq, j_lo = tid % kTq;
+    double2 lo_a = make_double2(1.0, 0.0), lo_b = lo_a;
     if (kRope) {
         if (tid < kPairs)
             sm.inv_freq[tid] = rope_inv_freq(rp.base, tid, 2 * kPairs);
         __syncthreads();
-        for (int idx = tid; idx < kTq * kPairs; idx += kThreads)
-            sm.lo_rot[idx / kTq][idx % kTq] = rope_sincos64(idx % kTq, sm.inv_freq[idx / kTq]);
+        lo_a = rope_sincos64(j_lo, sm.inv_freq[c_lo]);
+        lo_b = rope_sincos64(j_lo, sm.inv_freq[c_lo + kPairs / 2]);
     }
-    // hi_rot[buf] <- rotation by t * theta_c (t a multiple of 32), threads 0..31.
-    auto fill_hi = [&](int buf, int t) {
+    // hi_rot[t & 1] <- rotation by the base of tile t, threads 0..31.
+    auto fill_hi = [&](int t) {
         if (tid < kPairs)
-            sm.hi_rot[buf][tid] = rope_sincos64(t, sm.inv_freq[tid]);
+            sm.hi_rot[t & 1][tid] = rope_sincos64_call(t * kTq, sm.inv_freq[tid]);
     };
-    // (cos, sin) of pairs c0..c0+3 of the token at offset j of the block whose
-    // rotation by its base position is hi[]
-    auto rot4 = [&](const double2 *hi, int j, int c0, float2 (&cs)[4]) {
+    // cs[buf] <- the table of the block whose base rotation is hi[]: two entries
+    // per thread (the entry indices are recomputed from an opaque copy of tid,
+    // not held in registers across the loop)
+    auto fill_table = [&](const double2 *hi, int buf) {
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        const int c = t / kTq, j = t % kTq;
+        sm.cs[buf][c][j] = rope_compose(hi[c], lo_a);
+        sm.cs[buf][c + kPairs / 2][j] = rope_compose(hi[c + kPairs / 2], lo_b);
+    };
+    // (cos, sin) of pairs c0..c0+3 of the token at offset j, from table buf
+    auto rot4 = [&](int buf, int j, int c0, float2 (&cs)[4]) {
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-            cs[p] = rope_compose(hi[c0 + p], sm.lo_rot[c0 + p][j]);
+            cs[p] = sm.cs[buf][c0 + p][j];
     };
 
     // ---- key blocks: global -> registers -> (rotate) -> LDS ring slot ----
@@ -164,10 +192,8 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
             kreg[1] = buf_load16(kbuf, rel * krow + kg_off[1]);
         vreg = buf_load16(vbuf, rel * vrow + vg_off);
     };
-    // hi: rotation table of the block's base position (rope only); own: this run
-    // writes k_rot
-    auto store_block = [&](int jb, const uint4 (&kreg)[2], const uint4 &vreg, const double2 *hi,
-                           bool own) {
+    // tab: table of the block's tokens (rope only); own: this run writes k_rot
+    auto store_block = [&](int jb, const uint4 (&kreg)[2], const uint4 &vreg, int tab, bool own) {
         const int slot = jb % kSlots;
         const uint32_t rel = (uint32_t)(jb * kKb - tbase);
 #pragma unroll
@@ -176,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
                 uint4 x = kreg[u];
                 if (kRope && k_d[u] < 8) {
                     float2 cs[4];
-                    rot4(hi, k_key[u], 4 * k_d[u], cs);
+                    rot4(tab, k_key[u], 4 * k_d[u], cs);
                     x = rope_chunk_bf16(x, cs);
                 }
                 *(uint4 *)&sm.k[slot][kl_off[u]] = x;
@@ -197,53 +223,66 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
         for (int s = 0; s < kDqk / 16; ++s)
             qr[s] = buf_load16(qbuf, off + (uint32_t)s * 32);
     };
-    auto rotate_q = [&](uint4 (&qr)[kDqk / 16], int cs_buf) {
+    auto rotate_q = [&](uint4 (&qr)[kDqk / 16], int tab) {
         if (kRope) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {  // dims < 64: chunks 2s+hh < 8
                 float2 cs[4];
-                rot4(sm.hi_rot[cs_buf], r, 4 * (2 * s + hh), cs);
+                rot4(tab, r, 4 * (2 * s + hh), cs);
                 qr[s] = rope_chunk_bf16(qr[s], cs);
             }
         }
     };
 
-    // ---- prologue: the first tile's window and Q; hi rotations of the next tiles ----
-    // hi_rot[i & 1] holds tile i's block; it is written two tiles ahead (at the
-    // end of tile i-2, or here) and published by that tile's closing barrier.
+    // ---- prologue: the first tile's window and Q ----
+    // Rotation schedule of the loop (tile i, all before its closing barrier): the
+    // new key block and the next Q are rotated with tile i+1's table; then every
+    // thread builds its entries of tile i+2's table from hi_rot of tile i+2, and
+    // threads 0..31 compute hi_rot of tile i+3.  The barrier publishes both, and
+    // the buffers written are the ones last read before the previous barrier.
     uint4 qcur[kDqk / 16];
     {
         // All of the first tile's window blocks are requested at once (one memory
-        // latency rather than one per block), their rotation tables computed side
-        // by side: block jhi (the tile's own) in hi_rot[cb], the others in hi_pro.
+        // latency rather than one per block), their base rotations computed side
+        // by side into hi_pro, those of the next two tiles into hi_rot.
         const int t0 = tile_begin * kTq;
         const int jlo = first_block(t0), jhi = t0 / kKb;
-        const int cb = tile_begin & 1;
         const int nb = jhi - jlo + 1;  // 1 .. kMaxWinBlocks
+        const int cb = tile_begin & 1;
         uint4 kr[kMaxWinBlocks][2], vr[kMaxWinBlocks];
 #pragma unroll
         for (int i = 0; i < kMaxWinBlocks; ++i)
             if (i < nb)
                 load_block(jlo + i, kr[i], vr[i]);
         load_q(t0, qcur);
-        if (kRope && tid < kPairs * nb) {
+        if (kRope) {
             const int i = tid / kPairs, c = tid % kPairs;
-            const double2 x = rope_sincos64((jlo + i) * kKb, sm.inv_freq[c]);
-            if (i == nb - 1)
-                sm.hi_rot[cb][c] = x;
-            else
-                sm.hi_pro[i][c] = x;
+            if (i < nb)
+                sm.hi_pro[i][c] = rope_sincos64((jlo + i) * kKb, sm.inv_freq[c]);
+            else if (i >= kMaxWinBlocks && i < kMaxWinBlocks + 2) {
+                const int t = tile_begin + 1 + (i - kMaxWinBlocks);
+                if (t < tile_end)
+                    sm.hi_rot[t & 1][c] = rope_sincos64(t * kTq, sm.inv_freq[c]);
+            }
+            __syncthreads();
+            if (tile_begin + 1 < tile_end)
+                fill_table(sm.hi_rot[cb ^ 1], cb ^ 1);
         }
-        __syncthreads();
+        // window blocks one at a time through table cb (with RoPE): build, sync,
+        // rotate and store, sync
 #pragma unroll
         for (int i = 0; i < kMaxWinBlocks; ++i)
-            if (i < nb)
-                store_block(jlo + i, kr[i], vr[i], i == nb - 1 ? sm.hi_rot[cb] : sm.hi_pro[i],
-                            i == nb - 1);
-        rotate_q(qcur, cb);
-        __syncthreads();
-        if (kRope && tile_begin + 1 < tile_end)
-            fill_hi(cb ^ 1, t0 + kTq);
+            if (i < nb) {
+                if (kRope) {
+                    fill_table(sm.hi_pro[i], cb);
+                    __syncthreads();
+                }
+                store_block(jlo + i, kr[i], vr[i], cb, i == nb - 1);
+                if (i == nb - 1)
+                    rotate_q(qcur, cb);
+                if (kRope)
+                    __syncthreads();
+            }
         __syncthreads();
     }
 
@@ -345,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
         // wait on the prefetch can also end up waiting on the stores.
         if (has_next) {
             const int nb = (tile + 1) & 1;  // table of the next tile's tokens
-            store_block(jhi + 1, kreg, vreg, sm.hi_rot[nb], true);
+            store_block(jhi + 1, kreg, vreg, nb, true);
             rotate_q(qnext, nb);
         }
 
@@ -374,8 +413,12 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
 #pragma unroll
             for (int s = 0; s < kDqk / 16; ++s)
                 qcur[s] = qnext[s];
-            if (kRope && tile + 2 < tile_end)
-                fill_hi(tile & 1, t0 + 2 * kTq);
+        }
+        if (kRope) {
+            if (tile + 2 < tile_end)
+                fill_table(sm.hi_rot[tile & 1], tile & 1);
+            if (tile + 3 < tile_end)
+                fill_hi(tile + 3);
         }
         __syncthreads();
     }
