@@ -16,6 +16,10 @@
 //     tile (a 32-token tile sees 159 keys);
 //   - while tile i is computed, the next tile's Q (into registers) and its new
 //     key block (into registers, then into the free ring slot) are in flight;
+//   - the next tile's Q is requested in two halves, at the start of the tile
+//     and after its third key block, so the loads reach HBM over most of the
+//     tile rather than in one burst at its start (the memory otherwise idled
+//     while the tile's last blocks were computed);
 //   - one barrier per tile publishes the new key block;
 //   - with RoPE, the fp32 (cos, sin) of a tile's 32 tokens are composed once per
 //     tile into an LDS table (two entries per thread) that the Q of all 8 heads
@@ -53,6 +57,7 @@ constexpr int kKChunks = kKb * kDqk / 8;  // 768 16-byte pieces per key block
 constexpr int kVChunks = kKb * kDv / 8;   // 512
 constexpr int kPairs = 32;          // rope_dim / 2 with rope_dim = 64
 constexpr int kMaxWinBlocks = kSlots - 1;  // key blocks a tile's window spans (W <= 129)
+constexpr int kQSplit = 3;  // key blocks after which the second half of the next Q is requested
 static_assert(kVChunks == kThreads, "one V piece per thread");
 
 // RoPE.  A position splits as p = 32*floor(p/32) + (p mod 32); its (cos, sin)
@@ -169,59 +174,71 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
     // Per-thread offsets, computed once: K pieces c = tid, tid + 512 (key c/24, dims
     // (c%24)*8..+7); V piece of v_stage_coords.  Output dim
     // 8*dc + j sits in V^T row vrow0 + 32*(j/4) + j%4 (see pv_row_of_dim).
+    // These per-thread coordinates are recomputed from an opaque copy of tid
+    // where a block is loaded or stored (a few integer operations per tile)
+    // instead of being held in ~10 registers across the score loop.
     const bool k2 = tid + kThreads < kKChunks;  // wave-uniform
-    uint32_t kg_off[2];
-    int kl_off[2], k_key[2], k_d[2];
+    struct Piece {
+        int k_key[2], k_d[2], v_kk, v_dc;
+    };
+    auto piece = [&]() {
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        Piece pc;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int c = min(tid + u * kThreads, kKChunks - 1);
-        k_key[u] = c / (kDqk / 8);
-        k_d[u] = c % (kDqk / 8);
-        kg_off[u] = (uint32_t)k_key[u] * krow + kcol + (uint32_t)k_d[u] * 16;
-        kl_off[u] = row_of_key(k_key[u]) * kKPitch + k_d[u] * 8;
-    }
-    int v_kk, v_dc;
-    v_stage_coords(tid, v_kk, v_dc);
-    const uint32_t vg_off = (uint32_t)v_kk * vrow + vcol + (uint32_t)v_dc * 16;
-    const int vl_off = pv_row_of_dim(v_dc * 8) * kVPitch + v_kk;
+        for (int u = 0; u < 2; ++u) {
+            const int c = min(t + u * kThreads, kKChunks - 1);
+            pc.k_key[u] = c / (kDqk / 8);
+            pc.k_d[u] = c % (kDqk / 8);
+        }
+        v_stage_coords(t, pc.v_kk, pc.v_dc);
+        return pc;
+    };
+    auto kg_off = [&](const Piece &pc, int u) {
+        return (uint32_t)pc.k_key[u] * krow + kcol + (uint32_t)pc.k_d[u] * 16;
+    };
 
     auto load_block = [&](int jb, uint4 (&kreg)[2], uint4 &vreg) {
+        const Piece pc = piece();
         const uint32_t rel = (uint32_t)(jb * kKb - tbase);
-        kreg[0] = buf_load16(kbuf, rel * krow + kg_off[0]);
+        kreg[0] = buf_load16(kbuf, rel * krow + kg_off(pc, 0));
         if (k2)
-            kreg[1] = buf_load16(kbuf, rel * krow + kg_off[1]);
-        vreg = buf_load16(vbuf, rel * vrow + vg_off);
+            kreg[1] = buf_load16(kbuf, rel * krow + kg_off(pc, 1));
+        vreg = buf_load16(vbuf, (rel + (uint32_t)pc.v_kk) * vrow + vcol + (uint32_t)pc.v_dc * 16);
     };
     // tab: table of the block's tokens (rope only); own: this run writes k_rot
     auto store_block = [&](int jb, const uint4 (&kreg)[2], const uint4 &vreg, int tab, bool own) {
+        const Piece pc = piece();
         const int slot = jb % kSlots;
         const uint32_t rel = (uint32_t)(jb * kKb - tbase);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             if (u == 0 || k2) {
                 uint4 x = kreg[u];
-                if (kRope && k_d[u] < 8) {
+                if (kRope && pc.k_d[u] < 8) {
                     float2 cs[4];
-                    rot4(tab, k_key[u], 4 * k_d[u], cs);
+                    rot4(tab, pc.k_key[u], 4 * pc.k_d[u], cs);
                     x = rope_chunk_bf16(x, cs);
                 }
-                *(uint4 *)&sm.k[slot][kl_off[u]] = x;
+                *(uint4 *)&sm.k[slot][row_of_key(pc.k_key[u]) * kKPitch + pc.k_d[u] * 8] = x;
                 if (kRope && write_krot && own)
-                    buf_store16(krbuf, rel * krow + kg_off[u], x);
+                    buf_store16(krbuf, rel * krow + kg_off(pc, u), x);
             }
         }
         const uint32_t w[4] = {vreg.x, vreg.y, vreg.z, vreg.w};
-        uint16_t *vt = &sm.vt[slot][vl_off];
+        uint16_t *vt = &sm.vt[slot][pv_row_of_dim(pc.v_dc * 8) * kVPitch + pc.v_kk];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             vt[(32 * (j >> 2) + (j & 3)) * kVPitch] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
     };
     // Q^T operand of one tile: k-step s, half hh -> dims (2s+hh)*8 .. +7 of token t0+r.
-    auto load_q = [&](int t0, uint4 (&qr)[kDqk / 16]) {
+    // k-steps [s_lo, s_hi) of it
+    auto load_q = [&](int t0, uint4 (&qr)[kDqk / 16], int s_lo, int s_hi) {
         const uint32_t off = (uint32_t)(t0 + r - tbase) * qrow + qcol + (uint32_t)hh * 16;
 #pragma unroll
         for (int s = 0; s < kDqk / 16; ++s)
-            qr[s] = buf_load16(qbuf, off + (uint32_t)s * 32);
+            if (s >= s_lo && s < s_hi)
+                qr[s] = buf_load16(qbuf, off + (uint32_t)s * 32);
     };
     auto rotate_q = [&](uint4 (&qr)[kDqk / 16], int tab) {
         if (kRope) {
@@ -254,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
         for (int i = 0; i < kMaxWinBlocks; ++i)
             if (i < nb)
                 load_block(jlo + i, kr[i], vr[i]);
-        load_q(t0, qcur);
+        load_q(t0, qcur, 0, kDqk / 16);
         if (kRope) {
             const int i = tid / kPairs, c = tid % kPairs;
             if (i < nb)
@@ -294,10 +311,12 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
         const int jlo = first_block(t0), jhi = t0 / kKb;
         const bool has_next = tile + 1 < tile_end;
 
+        // The next tile's Q is requested in two halves, the second after the
+        // first kQSplit key blocks (see the header).
         uint4 kreg[2], vreg, qnext[kDqk / 16];
         if (has_next) {
             load_block(jhi + 1, kreg, vreg);
-            load_q(t0 + kTq, qnext);
+            load_q(t0 + kTq, qnext, 0, kDqk / 32);
         }
 
         float m = sink2;
@@ -311,6 +330,8 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
             const int kb = jb * kKb;
             const uint16_t *ks = sm.k[jb % kSlots];
             const uint16_t *vs = sm.vt[jb % kSlots];
+            if (has_next && jb == jlo + kQSplit)
+                load_q(t0 + kTq, qnext, kDqk / 32, kDqk / 16);
             f32x16 sc = f32x16{};
             // K operands are read from LDS 4 k-steps at a time: the fence keeps the
             // scheduler from hoisting all 12 reads (48 registers) above the MFMAs.
@@ -380,6 +401,8 @@ __global__ __launch_bounds__(kThreads) void prefill_swa_kernel(PrefillArgs a, Sw
             __builtin_amdgcn_s_setprio(0);
         }
 
+        if (has_next && jhi < jlo + kQSplit)  // windows of fewer blocks
+            load_q(t0 + kTq, qnext, kDqk / 32, kDqk / 16);
         // The prefetched key block and Q are consumed before O is stored, so no
         // wait on the prefetch can also end up waiting on the stores.
         if (has_next) {
