@@ -525,6 +525,10 @@ hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s) {
         const hipError_t e16 = launch_decode16(a, s);
         if (e16 != hipSuccess)
             return e16;
+    } else if (!a.ring && a.window <= 0 && n_cols > 32) {
+        const hipError_t el = launch_verify_lds(a, s);
+        if (el != hipSuccess)
+            return el;
     } else if (n_cols <= 32) {
         if (a.rope)
             cached_bf16_kernel<1, true><<<grid, block, 0, s>>>(a, scale_log2);

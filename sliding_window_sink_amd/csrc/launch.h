@@ -82,6 +82,9 @@ hipError_t launch_cached_bf16(const CachedArgs &a, hipStream_t s);
 // Attention part of launch_cached_bf16 for at most 16 columns per KV group
 // (no split-K combine).
 hipError_t launch_decode16(const CachedArgs &a, hipStream_t s);
+// Attention part of launch_cached_bf16 for 17..64 columns per KV group over a
+// contiguous bf16 cache without a window (K/V staged in LDS; no combine).
+hipError_t launch_verify_lds(const CachedArgs &a, hipStream_t s);
 hipError_t launch_cached_f32(const CachedArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int bf16, hipStream_t s);
 hipError_t launch_advance_len(int32_t *cache_len, const int32_t *n_accept, int B, int n,
