@@ -23,13 +23,15 @@
 //                    key 16hh + i; dP^T = V dO^T with V rows permuted the same
 //                    way; dQ^T += K^T dS^T with the K^T operand read from the
 //                    same K rows by gfx950's transposing LDS loads.
-//   bwd_dkdv_kernel  per (KV group, 32-key block), 4 waves: S = Q K^T with each
-//                    lane owning a key column and Q rows permuted so C-register i
-//                    of half hh is query 16hh + i, so P and dS are directly the
-//                    B operands of dV^T += dO^T P and dK^T += Q^T dS; Q and dO
-//                    rows go to a per-wave row-major LDS tile whose transposing
-//                    reads give the Q^T / dO^T operands; the 4 waves (disjoint
-//                    heads) are summed through LDS in a fixed order at the end.
+//   bwd_dkdv_kernel  per (KV group, 64-key block), 4 waves of 16 keys each, every
+//                    query head of the group: 16x16x32 products, S = Q K^T with
+//                    each lane owning a key column and Q rows permuted so the C
+//                    registers of a lane hold 8 consecutive queries, so P and dS
+//                    are directly the B operands of dV^T += dO^T P and
+//                    dK^T += Q^T dS; the step's Q and dO tile is shared by the
+//                    4 waves, put into LDS two steps ahead by global->LDS loads
+//                    in MFMA operand order (the Q^T / dO^T operands come from
+//                    the same pieces through transposing reads).
 // Every output element is written once (no atomics): results are deterministic.
 #include "common.h"
 #include "lds_tr.h"
@@ -268,227 +270,258 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
 
 // ------------------------------------------------------------------ dK, dV
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4v mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4v &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 constexpr int kKWaves = 4;
 constexpr int kKThreads = kKWaves * 64;
-constexpr int kQRPitch = kDqk + 8;  // per-wave Q rows (bf16): 400 bytes
-constexpr int kGRPitch = kDv + 8;   // per-wave dO rows (bf16): 272 bytes
-constexpr int kRedPitch = kKb + 1;  // fp32 reduction rows
+constexpr int kKPerWave = 16;                     // keys per wave (16x16x32 tiles)
+constexpr int kKBlk = kKWaves * kKPerWave;        // keys per workgroup
+constexpr int kQPieces = 2 * (kDqk / 32);         // 12 pieces of 1 KB: Q tile
+constexpr int kGPieces = 2 * (kDv / 32);          // 8: dO tile
+constexpr int kTilePieces = kQPieces + kGPieces;  // 20
+constexpr int kStepBytes = kTilePieces * 1024;
+constexpr int kStepLoads = kTilePieces / kKWaves + 2;  // global->LDS loads per thread per step
+static_assert(kQPieces % kKWaves == 0 && kGPieces % kKWaves == 0, "uniform piece split");
 
-struct DkvSmem {
-    union {
-        struct {
-            uint16_t qr[kKWaves][kTq * kQRPitch];
-            uint16_t gr[kKWaves][kTq * kGRPitch];
-        } w;
-        float red[2][(kDqk + kDv) * kRedPitch];
-    };
-};
+// One global->LDS load per wave: lane l's 16 (4) bytes at r + off land at
+// lds + 16 l (4 l).
+__device__ __forceinline__ void lds_load16(BufRsrc r, uint8_t *lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             off, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(BufRsrc r, uint8_t *lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4,
+                                             off, 0, 0, 0);
+}
+// Wait until at most N vector memory operations of this thread are outstanding
+// (kLds: and none of its LDS operations).
+template <int N, bool kLds = false>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((kLds ? 0 : 0xF) << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
+// dK, dV of one 64-key block of KV group g.  Wave w owns keys kb + 16w .. +15 and
+// keeps their dK^T / dV^T (80 accumulators per lane) over every query head of
+// the group and every 32-query tile that sees the block; the four waves share
+// each step's Q and dO tile, which global->LDS loads (no registers held) put
+// into a ring of three LDS slots two steps ahead, so a wave fits in ~200
+// registers and two waves share a SIMD.  Lane l: lr = l % 16, lg = l / 16.
+//   Tile layout: 1 KB pieces in 16x16x32 A-operand order -- Q piece 6mt + s,
+//   lane l holds query pq(mt, l%16) = 8((l%16)/4) + 4mt + (l%16)%4 of the tile,
+//   dims 32s + 8(l/16) .. +7 (dO likewise, 4 pieces per half) -- so the A
+//   operands of S = Q K^T and dP = dO V^T are conflict-free 16-byte reads and
+//   their C registers hold queries 8lg .. 8lg+7 (register i of half mt: query
+//   8lg + 4mt + i) of key lr: exactly the B operand (k = queries) of
+//   dV^T += dO^T P and dK^T += Q^T dS.  The dO^T / Q^T operands (row = dim, k =
+//   queries 8lg ..) are read from the same pieces by gfx950's transposing loads
+//   (each 16-lane group touches 512 contiguous bytes: no bank conflicts).
+//   K and V of the wave's 16 keys stay in registers as the B operands.
+// Every thread issues exactly 7 global->LDS loads per step (5 tile pieces; its
+// wave's own copy of the tile's lse and D), so "at most 7 outstanding" before a
+// step's barrier means its part of that step has landed.  The slots are separate LDS arrays named statically
+// in a loop unrolled by three (the compiler's wait counts can then tell them
+// apart), and steps past the last load past-the-end offsets (zeros, no memory
+// access).
 template <bool kWindowed>
-__global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a, int n_units, int n_blk,
-                                                             float scale_log2) {
-    __shared__ DkvSmem sm;
+__global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n_units, int n_blk,
+                                                                float scale_log2) {
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[kStepBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[kStepBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[kStepBytes];
+    // per slot, the tile's lse (floats 0..31) and D (64..95), one copy per wave
+    __shared__ __attribute__((aligned(16))) float ls0[kKWaves][128];
+    __shared__ __attribute__((aligned(16))) float ls1[kKWaves][128];
+    __shared__ __attribute__((aligned(16))) float ls2[kKWaves][128];
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, window = a.window;
     const int group = Hq / Hkv;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r = lane & 31, hh = lane >> 5;
+    const int lr = lane & 15, lg = lane >> 4;
     const int unit = blockIdx.x % n_units;
     const int blk = blockIdx.x / n_units;  // ascending: key block 0 sees the most queries
     const int g = unit % Hkv, b = unit / Hkv;
-    const int kb = blk * kKb;
-    const int key = kb + r;  // this lane's key column
+    const int kb = blk * kKBlk;
+    const int kw = kb + kKPerWave * wave;  // this wave's first key
+    const int key = kw + lr;               // this lane's key column
+    if (kb >= T)
+        return;  // uniform
+
+    // queries that can see some key of the block: [kb, last]
+    const int last = kWindowed ? min(T - 1, kb + kKBlk - 1 + window - 1) : T - 1;
+    const int n_tiles = (last - kb) / kTq + 1;
+    const int n_steps = group * n_tiles;  // step = (head of the group, query tile)
 
     const size_t row0 = (size_t)b * T;
     const uint32_t qrow = (uint32_t)Hq * kDqk * 2, orow = (uint32_t)Hq * kDv * 2;
     const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
     const BufRsrc qbuf = make_buf((const uint16_t *)a.q + row0 * Hq * kDqk, (uint64_t)T * qrow);
     const BufRsrc gbuf = make_buf((const uint16_t *)a.dout + row0 * Hq * kDv, (uint64_t)T * orow);
-    const BufRsrc kbuf = make_buf((const uint16_t *)a.k + row0 * Hkv * kDqk, (uint64_t)T * krow);
-    const BufRsrc vbuf = make_buf((const uint16_t *)a.v + row0 * Hkv * kDv, (uint64_t)T * vrow);
+    const BufRsrc lbuf = make_buf(a.lse + (size_t)b * Hq * T, (uint64_t)Hq * T * 4);
+    const BufRsrc dbuf = make_buf(a.D + (size_t)b * Hq * T, (uint64_t)Hq * T * 4);
 
-    // B operands for the whole block: K^T and V^T columns = this lane's key.
-    uint4 kf[kDqk / 16], vf[kDv / 16];
+    // B operands: K (k-step s: dims 32s + 8lg .. +7 of key lr) and V, for the whole kernel
+    uint4 kr[kDqk / 32], vr[kDv / 32];
     {
-        const uint32_t ko = (uint32_t)key * krow + (uint32_t)g * kDqk * 2 + (uint32_t)hh * 16;
-        const uint32_t vo = (uint32_t)key * vrow + (uint32_t)g * kDv * 2 + (uint32_t)hh * 16;
+        const BufRsrc kbuf = make_buf((const uint16_t *)a.k + row0 * Hkv * kDqk, (uint64_t)T * krow);
+        const BufRsrc vbuf = make_buf((const uint16_t *)a.v + row0 * Hkv * kDv, (uint64_t)T * vrow);
+        const uint32_t ko = key < T ? (uint32_t)key * krow + (uint32_t)g * kDqk * 2 + (uint32_t)lg * 16 : kOob;
+        const uint32_t vo = key < T ? (uint32_t)key * vrow + (uint32_t)g * kDv * 2 + (uint32_t)lg * 16 : kOob;
 #pragma unroll
-        for (int s = 0; s < kDqk / 16; ++s)
-            kf[s] = buf_load16(kbuf, ko + (uint32_t)s * 32);
+        for (int s = 0; s < kDqk / 32; ++s)
+            kr[s] = buf_load16(kbuf, ko + (uint32_t)s * 64);
 #pragma unroll
-        for (int s = 0; s < kDv / 16; ++s)
-            vf[s] = buf_load16(vbuf, vo + (uint32_t)s * 32);
+        for (int s = 0; s < kDv / 32; ++s)
+            vr[s] = buf_load16(vbuf, vo + (uint32_t)s * 64);
     }
 
-    f32x16 dk[kDqk / 32], dv[kDv / 32];
+    // This thread's 7 loads of step k into a slot (offsets with bit 31 set read
+    // nothing; every real offset is below 2^31).
+    const int pq_lane = 8 * (lr >> 2) + (lr & 3);  // + 4mt: query of A row lr
+    auto load_step = [&](uint8_t *slot, int k) {
+        const uint32_t step_oob = k < n_steps ? 0u : kOob;
+        const int kk = k < n_steps ? k : 0;
+        const int h = g * group + kk / n_tiles;
+        const int q0 = kb + (kk % n_tiles) * kTq;
 #pragma unroll
-    for (int d = 0; d < kDqk / 32; ++d)
-        dk[d] = f32x16{};
-#pragma unroll
-    for (int d = 0; d < kDv / 32; ++d)
-        dv[d] = f32x16{};
-
-    // queries that can see some key of the block: [kb, last]
-    const int last = kWindowed ? min(T - 1, kb + kKb - 1 + window - 1) : T - 1;
-    const int n_tiles = kb < T ? (last - kb) / kTq + 1 : 0;
-    const int qrow_r = key_of_row(r);  // A-row r of a tile holds query q0 + key_of_row(r)
-    uint16_t *qt = sm.w.qr[wave], *gt = sm.w.gr[wave];
-    // Q^T / dO^T operands through transposing reads of the row-major tiles: source
-    // lane 4e'+q of group G points at query 16hh + 8t + 4L + e' and dims
-    // 32d + 16(G%2) + 4q .. +3 (A-row r = dim 32d + r)
-    int qt_off[2][2], gt_off[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int L = 0; L < 2; ++L) {
-            const int qq = 16 * hh + 8 * t + 4 * L + ((lane & 15) >> 2);
-            const int dd = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            qt_off[t][L] = qq * kQRPitch + dd;
-            gt_off[t][L] = qq * kGRPitch + dd;
+        for (int u = 0; u < kQPieces / kKWaves; ++u) {
+            const int pc = wave + kKWaves * u;
+            const int mt = pc / 6, s = pc % 6;
+            const int q = q0 + pq_lane + 4 * mt;
+            const uint32_t off = ((uint32_t)q * qrow + (uint32_t)h * kDqk * 2 + (uint32_t)(32 * s + 8 * lg) * 2) |
+                                 step_oob | (q < T ? 0u : kOob);
+            lds_load16(qbuf, slot + pc * 1024, off);
         }
-
-    for (int hi = wave; hi < group; hi += kKWaves) {
-        const int h = g * group + hi;
-        const float *lse_h = a.lse + ((size_t)b * Hq + h) * T;
-        const float *D_h = a.D + ((size_t)b * Hq + h) * T;
-        const BufRsrc lbuf = make_buf(lse_h, (uint64_t)T * 4);
-        const BufRsrc dbuf = make_buf(D_h, (uint64_t)T * 4);
-        for (int it = 0; it < n_tiles; ++it) {
-            const int q0 = kb + it * kTq;
-            const int qa_row = q0 + qrow_r;
-            uint4 qa[kDqk / 16], ga[kDv / 16];
-            {
-                const uint32_t qo = qa_row < T ? (uint32_t)qa_row * qrow + (uint32_t)h * kDqk * 2 +
-                                                     (uint32_t)hh * 16
-                                               : kOob;
-                const uint32_t go = qa_row < T ? (uint32_t)qa_row * orow + (uint32_t)h * kDv * 2 +
-                                                     (uint32_t)hh * 16
-                                               : kOob;
 #pragma unroll
-                for (int s = 0; s < kDqk / 16; ++s)
-                    qa[s] = buf_load16(qbuf, qo + (uint32_t)s * 32);
-#pragma unroll
-                for (int s = 0; s < kDv / 16; ++s)
-                    ga[s] = buf_load16(gbuf, go + (uint32_t)s * 32);
-            }
-            // lse and D of the 16 queries q0 + 16hh + i this lane's registers hold
-            float ls[16], dd[16];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t off = (uint32_t)(q0 + 16 * hh + 4 * c) * 4;
-                const uint4 l4 = buf_load16(lbuf, off), d4 = buf_load16(dbuf, off);
-                ls[4 * c + 0] = __builtin_bit_cast(float, l4.x);
-                ls[4 * c + 1] = __builtin_bit_cast(float, l4.y);
-                ls[4 * c + 2] = __builtin_bit_cast(float, l4.z);
-                ls[4 * c + 3] = __builtin_bit_cast(float, l4.w);
-                dd[4 * c + 0] = __builtin_bit_cast(float, d4.x);
-                dd[4 * c + 1] = __builtin_bit_cast(float, d4.y);
-                dd[4 * c + 2] = __builtin_bit_cast(float, d4.z);
-                dd[4 * c + 3] = __builtin_bit_cast(float, d4.w);
-            }
-            // Q and dO rows of the tile into this wave's LDS, queries in natural order
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int s = 0; s < kDqk / 16; ++s)
-                *(uint4 *)&qt[qrow_r * kQRPitch + (2 * s + hh) * 8] = qa[s];
-#pragma unroll
-            for (int s = 0; s < kDv / 16; ++s)
-                *(uint4 *)&gt[qrow_r * kGRPitch + (2 * s + hh) * 8] = ga[s];
-            // S = Q K^T and dP = dO V^T: column = key, register i = query q0 + 16hh + i
-            f32x16 sc = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int s = 0; s < kDqk / 16; ++s)
-                sc = mfma32x32x16(as_bf16x8(qa[s]), as_bf16x8(kf[s]), sc);
-#pragma unroll
-            for (int s = 0; s < kDv / 16; ++s)
-                dp = mfma32x32x16(as_bf16x8(ga[s]), as_bf16x8(vf[s]), dp);
-            bf16x8 pb[2], sb[2];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int q = q0 + 16 * hh + i;
-                const bool vis = q < T && key <= q && (!kWindowed || q - key < window);
-                const float p = vis ? fast_exp2(__fmaf_rn(sc[i], scale_log2, -ls[i] * kLog2e)) : 0.f;
-                pb[i >> 3][i & 7] = (__bf16)p;
-                sb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dd[i]));
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // dV^T += dO^T P, dK^T += Q^T dS: A rows = dims, step t = queries 16hh + 8t ..
-#pragma unroll
-            for (int d = 0; d < kDv / 32; ++d)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const uint2 lo = lds_tr16(gt + gt_off[t][0] + 32 * d);
-                    const uint2 hi = lds_tr16(gt + gt_off[t][1] + 32 * d);
-                    dv[d] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[t], dv[d]);
-                }
-#pragma unroll
-            for (int d = 0; d < kDqk / 32; ++d)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const uint2 lo = lds_tr16(qt + qt_off[t][0] + 32 * d);
-                    const uint2 hi = lds_tr16(qt + qt_off[t][1] + 32 * d);
-                    dk[d] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), sb[t], dk[d]);
-                }
+        for (int u = 0; u < kGPieces / kKWaves; ++u) {
+            const int pc = wave + kKWaves * u;
+            const int mt = pc / 4, s = pc % 4;
+            const int q = q0 + pq_lane + 4 * mt;
+            const uint32_t off = ((uint32_t)q * orow + (uint32_t)h * kDv * 2 + (uint32_t)(32 * s + 8 * lg) * 2) |
+                                 step_oob | (q < T ? 0u : kOob);
+            lds_load16(gbuf, slot + (kQPieces + pc) * 1024, off);
         }
-    }
+    };
+    // the tile's lse and D of step k into this wave's copy in a slot
+    auto load_ld = [&](float (*ls)[128], int k) {
+        const uint32_t step_oob = k < n_steps ? 0u : kOob;
+        const int kk = k < n_steps ? k : 0;
+        const int h = g * group + kk / n_tiles;
+        const int q = kb + (kk % n_tiles) * kTq + lane;  // lanes 0..31: the tile's queries
+        const uint32_t off = ((uint32_t)h * T + (uint32_t)q) * 4 | step_oob |
+                             (lane < kTq && q < T ? 0u : kOob);
+        lds_load4(lbuf, (uint8_t *)ls[wave], off);
+        lds_load4(dbuf, (uint8_t *)&ls[wave][64], off);
+    };
 
-    // Sum the 4 waves' partials in the fixed order (w0 + w2) + (w1 + w3) through two
-    // LDS regions: waves 0 and 1 store theirs, waves 2 and 3 then add theirs into
-    // region wave & 1 (every read of a lane issued before its writes, so the wave
-    // pays one LDS latency rather than one per element), and the row writer adds
-    // the two regions.
-    float *red = sm.red[wave & 1];
-    auto red_at = [&](int row) -> float & { return red[row * kRedPitch + r]; };
-    __syncthreads();
-    if (wave < 2) {
+    f32x4v dk[kDqk / 16], dv[kDv / 16];  // C tiles: rows dims 16dt + 4lg + i, column key lr
 #pragma unroll
-        for (int d = 0; d < kDqk / 32; ++d)
+    for (int d = 0; d < kDqk / 16; ++d)
+        dk[d] = f32x4v{};
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                red_at(32 * d + c_row(i, hh)) = dk[d][i];
+    for (int d = 0; d < kDv / 16; ++d)
+        dv[d] = f32x4v{};
+
+    // transposing-read source of this lane inside a half's pieces: tile row
+    // (query) 8lg + lr/4 (+4 in half 1), dims 16dt + 4(lr%4) .. +3
+    const int tr_off = 16 * (4 * lg + (lr >> 2) + 16 * ((lr & 3) >> 1)) + 8 * (lr & 1);
+
+    auto compute = [&](const uint8_t *slot, const float (*ls)[128], int k) {
+        const int q0 = kb + (k % n_tiles) * kTq;
+        // does any (query, key) pair of the tile and this wave's keys count?
+        const bool act = q0 + kTq - 1 >= kw && (!kWindowed || q0 <= kw + kKPerWave - 1 + window - 1);
+        if (!act)
+            return;  // wave-uniform
+        const uint8_t *qs = slot, *gs = slot + kQPieces * 1024;
+        f32x4v sc[2] = {f32x4v{}, f32x4v{}}, dp[2] = {f32x4v{}, f32x4v{}};
 #pragma unroll
-        for (int d = 0; d < kDv / 32; ++d)
+        for (int s = 0; s < kDqk / 32; ++s)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                red_at(kDqk + 32 * d + c_row(i, hh)) = dv[d][i];
+            for (int mt = 0; mt < 2; ++mt)
+                sc[mt] = mfma16x16x32(as_bf16x8(*(const uint4 *)(qs + (6 * mt + s) * 1024 + lane * 16)),
+                                      as_bf16x8(kr[s]), sc[mt]);
+#pragma unroll
+        for (int s = 0; s < kDv / 32; ++s)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                dp[mt] = mfma16x16x32(as_bf16x8(*(const uint4 *)(gs + (4 * mt + s) * 1024 + lane * 16)),
+                                      as_bf16x8(vr[s]), dp[mt]);
+        // P and dS of this lane's 8 queries (element j = query q0 + 8lg + j)
+        const float *ld = ls[wave];
+        const float4 l0 = *(const float4 *)(ld + 8 * lg), l1 = *(const float4 *)(ld + 8 * lg + 4);
+        const float4 d0 = *(const float4 *)(ld + 64 + 8 * lg), d1 = *(const float4 *)(ld + 64 + 8 * lg + 4);
+        const float lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const float dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+        bf16x8 pb, sb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int q = q0 + 8 * lg + j;
+            const bool vis = q < T && key <= q && (!kWindowed || q - key < window);
+            const float sv = sc[j >> 2][j & 3], dpv = dp[j >> 2][j & 3];
+            const float p = vis ? fast_exp2(__fmaf_rn(sv, scale_log2, -lw[j] * kLog2e)) : 0.f;
+            pb[j] = (__bf16)p;
+            sb[j] = (__bf16)(p * (dpv - dw[j]));
+        }
+        // dV^T += dO^T P (tile dt: dims 16dt ..; k-step = the tile's 32 queries)
+#pragma unroll
+        for (int dt = 0; dt < kDv / 16; ++dt) {
+            const uint8_t *src = gs + (dt >> 1) * 1024 + (dt & 1) * 512 + tr_off;
+            const uint2 x0 = lds_tr16((const uint16_t *)src);
+            const uint2 x1 = lds_tr16((const uint16_t *)(src + 4 * 1024));
+            dv[dt] = mfma16x16x32(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), pb, dv[dt]);
+        }
+        // dK^T += Q^T dS
+#pragma unroll
+        for (int dt = 0; dt < kDqk / 16; ++dt) {
+            const uint8_t *src = qs + (dt >> 1) * 1024 + (dt & 1) * 512 + tr_off;
+            const uint2 x0 = lds_tr16((const uint16_t *)src);
+            const uint2 x1 = lds_tr16((const uint16_t *)(src + 6 * 1024));
+            dk[dt] = mfma16x16x32(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), sb, dk[dt]);
+        }
+    };
+
+    // Step k: wait for this thread's loads of step k (step k+1's seven may still
+    // be in flight), barrier (every thread's part of step k is in, and every
+    // wave is done with step k-1, whose slot receives step k+2), compute.
+    load_step(st0, 0);
+    load_ld(ls0, 0);
+    load_step(st1, 1);
+    load_ld(ls1, 1);
+    auto step = [&](int k, const uint8_t *cur, const float (*lcur)[128], uint8_t *next2,
+                    float (*lnext2)[128]) {
+        wait_vmem<kStepLoads>();
+        wg_barrier();
+        load_step(next2, k + 2);
+        load_ld(lnext2, k + 2);
+        if (k < n_steps)
+            compute(cur, lcur, k);
+    };
+    for (int k = 0; k < n_steps; k += 3) {
+        step(k, st0, ls0, st2, ls2);
+        step(k + 1, st1, ls1, st0, ls0);
+        step(k + 2, st2, ls2, st1, ls1);
     }
-    __syncthreads();
-    if (wave >= 2) {
-        float pk[kDqk / 32][16], pv[kDv / 32][16];
+    wait_vmem<0>();  // no load into LDS outlives the workgroup
+
+    if (key < T) {
+        const size_t trow = (row0 + key) * Hkv + g;
 #pragma unroll
-        for (int d = 0; d < kDqk / 32; ++d)
+        for (int dt = 0; dt < kDqk / 16; ++dt) {
+            const f32x4v x = dk[dt] * a.scale;
+            *(float4 *)&a.dk[trow * kDqk + 16 * dt + 4 * lg] = make_float4(x[0], x[1], x[2], x[3]);
+        }
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                pk[d][i] = red_at(32 * d + c_row(i, hh));
-#pragma unroll
-        for (int d = 0; d < kDv / 32; ++d)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                pv[d][i] = red_at(kDqk + 32 * d + c_row(i, hh));
-#pragma unroll
-        for (int d = 0; d < kDqk / 32; ++d)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                red_at(32 * d + c_row(i, hh)) = pk[d][i] + dk[d][i];
-#pragma unroll
-        for (int d = 0; d < kDv / 32; ++d)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                red_at(kDqk + 32 * d + c_row(i, hh)) = pv[d][i] + dv[d][i];
-    }
-    __syncthreads();
-    for (int idx = tid; idx < kKb * (kDqk + kDv); idx += kKThreads) {
-        const int kk = idx / (kDqk + kDv), dim = idx % (kDqk + kDv);
-        if (kb + kk >= T)
-            continue;
-        const float x = sm.red[0][dim * kRedPitch + kk] + sm.red[1][dim * kRedPitch + kk];
-        const size_t trow = (row0 + kb + kk) * Hkv + g;
-        if (dim < kDqk)
-            a.dk[trow * kDqk + dim] = x * a.scale;
-        else
-            a.dv[trow * kDv + dim - kDqk] = x;
+        for (int dt = 0; dt < kDv / 16; ++dt)
+            *(float4 *)&a.dv[trow * kDv + 16 * dt + 4 * lg] =
+                make_float4(dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]);
     }
 }
 
@@ -517,7 +550,7 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int k_units = a.B * a.Hkv;
-    const int n_blk = (a.T + kKb - 1) / kKb;
+    const int n_blk = (a.T + kKBlk - 1) / kKBlk;
     const dim3 kgrid((unsigned)(k_units * n_blk));
     if (a.window > 0)
         bwd_dkdv_kernel<true><<<kgrid, dim3(kKThreads), 0, s>>>(a, k_units, n_blk, scale_log2);
