@@ -383,14 +383,27 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n
             vr[s] = buf_load16(vbuf, vo + (uint32_t)s * 64);
     }
 
+    // Step k -> (query head, first query of the tile).  Windowed layers: heads
+    // outer, tiles ascending (a neighbouring block reads the same tile two steps
+    // later, while it is still in L2).  Global layers: tiles descending from the
+    // last one, heads inner: every block of the group walks the same (head,
+    // tile) sequence from the top and only stops at a different place, so the
+    // workgroups resident at one time read the same tile at about the same time
+    // (one fetch from memory, L2 hits for the rest).
+    auto step_head = [&](int k) {
+        return g * group + (kWindowed ? k / n_tiles : k % group);
+    };
+    auto step_q0 = [&](int k) {
+        return kb + (kWindowed ? k % n_tiles : n_tiles - 1 - k / group) * kTq;
+    };
     // This thread's 7 loads of step k into a slot (offsets with bit 31 set read
     // nothing; every real offset is below 2^31).
     const int pq_lane = 8 * (lr >> 2) + (lr & 3);  // + 4mt: query of A row lr
     auto load_step = [&](uint8_t *slot, int k) {
         const uint32_t step_oob = k < n_steps ? 0u : kOob;
         const int kk = k < n_steps ? k : 0;
-        const int h = g * group + kk / n_tiles;
-        const int q0 = kb + (kk % n_tiles) * kTq;
+        const int h = step_head(kk);
+        const int q0 = step_q0(kk);
 #pragma unroll
         for (int u = 0; u < kQPieces / kKWaves; ++u) {
             const int pc = wave + kKWaves * u;
@@ -414,8 +427,8 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n
     auto load_ld = [&](float (*ls)[128], int k) {
         const uint32_t step_oob = k < n_steps ? 0u : kOob;
         const int kk = k < n_steps ? k : 0;
-        const int h = g * group + kk / n_tiles;
-        const int q = kb + (kk % n_tiles) * kTq + lane;  // lanes 0..31: the tile's queries
+        const int h = step_head(kk);
+        const int q = step_q0(kk) + lane;  // lanes 0..31: the tile's queries
         const uint32_t off = ((uint32_t)h * T + (uint32_t)q) * 4 | step_oob |
                              (lane < kTq && q < T ? 0u : kOob);
         lds_load4(lbuf, (uint8_t *)ls[wave], off);
@@ -435,7 +448,7 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n
     const int tr_off = 16 * (4 * lg + (lr >> 2) + 16 * ((lr & 3) >> 1)) + 8 * (lr & 1);
 
     auto compute = [&](const uint8_t *slot, const float (*ls)[128], int k) {
-        const int q0 = kb + (k % n_tiles) * kTq;
+        const int q0 = step_q0(k);
         // does any (query, key) pair of the tile and this wave's keys count?
         const bool act = q0 + kTq - 1 >= kw && (!kWindowed || q0 <= kw + kKPerWave - 1 + window - 1);
         if (!act)
