@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     constexpr int kMerge = kTok ? 0 : kWaves - 1;
     __shared__ __attribute__((aligned(16))) float merge[kTok ? 1 : kMerge][kCols][kMergeStride];
     __shared__ float2 rope_tab[(kTok ? kMaxNqTok : kMaxNq) * 32];
+    __shared__ uint4 new_row[(kDqk + kDv) / 8];  // one new token's k, v rows (merged block)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, kg = lane >> 4;
@@ -147,7 +148,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     const int ce = min(rhi, P);
     const int n_cache_blk = ce > rlo ? (ce - rlo + kKb - 1) / kKb : 0;
     const int new_lo = max(rlo, P);
-    const int nblk = n_cache_blk + (rhi > new_lo ? 1 : 0);
+    // One new token whose position falls inside the last cache block's 32-key span
+    // (a ring layer's window of 128 keys: 127 cached + the new one) is computed as
+    // part of that block instead of as a block of its own: the wave that takes
+    // the block stages the token's k (rotated when RoPE is fused) and v rows in
+    // LDS, and the lanes holding key P take their operands from there (the cache
+    // loads of position P read nothing).  bf16 caches, waves splitting the blocks.
+    const bool merge_new = !kTok && !kFp8 && nq == 1 && n_cache_blk > 0 && rhi > new_lo &&
+                           P < rlo + n_cache_blk * kKb;
+    const int nblk = n_cache_blk + (rhi > new_lo && !merge_new ? 1 : 0);
     const int window = a.window;
     const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
 
@@ -215,6 +224,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // The wave's first cache block is requested before the RoPE table and the
     // new-token store, so its memory latency overlaps that work (the store
     // writes position P, which no cache block reads).
+    const bool merge_wave = merge_new && (n_cache_blk - 1) % kWaves == wave;  // wave-uniform
+    uint4 nk = make_uint4(0u, 0u, 0u, 0u), nv = nk;  // lane l: piece l of the new k / v row
+    if (merge_wave) {
+        nk = buf_load16(kn, lane < kDqk / 8 ? (uint32_t)lane * 16 : kOob);
+        nv = buf_load16(vn, lane < kDv / 8 ? (uint32_t)lane * 16 : kOob);
+    }
     KVc x;
     if constexpr (kTok) {
         if (kCols * wave < n_cols && n_cache_blk > 0) {
@@ -241,6 +256,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             cached_store_new<false, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
     }
 
+    if (merge_wave) {  // wave-private: the same wave reads the rows back (LDS keeps its order)
+        if (lane < kDqk / 8) {
+            uint4 v = nk;
+            if (a.rope && lane < 8)
+                v = rope_chunk_bf16(v, rope_tab + 4 * lane);
+            new_row[lane] = v;
+        }
+        if (lane < kDv / 8)
+            new_row[kDqk / 8 + lane] = nv;
+    }
+
     bf16x8 qf[kDqk / 32];
     if (a.rope && col_ok) {  // k-steps 0, 1 hold dims < 64: 8-dim chunk kdim0/8
         const float2 *cs = rope_tab + (col / group) * 32;
@@ -264,7 +290,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
         constexpr bool kCacheRegs = std::is_same<std::decay_t<decltype(x)>, KVc>::value;
         constexpr bool kScaled = kFp8 && kCacheRegs;  // E4M3 codes: fold the scales in
         const int kb = block_base(j);
-        const int kend = j < n_cache_blk ? ce : rhi;
+        const bool merged = kCacheRegs && merge_new && j == n_cache_blk - 1;
+        const int kend = j < n_cache_blk && !merged ? ce : rhi;
+        if constexpr (kCacheRegs && !kFp8) {
+            if (merged) {  // lanes holding key P take its operands from the staged rows
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    if (kb + 16 * kt + lr == P) {
+#pragma unroll
+                        for (int s = 0; s < kDqk / 32; ++s)
+                            x.k[kt][s] = new_row[kdim0<false>(s, kg) / 8];
+                    }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (kb + (e >> 2) * 16 + 4 * kg + (e & 3) == P)
+                        x.v[e] = new_row[kDqk / 8 + lr];
+            }
+        }
         const float sl2 = kScaled ? scale_log2 * a.k_scale : scale_log2;
         f32x4v sc[2];
 #pragma unroll
@@ -279,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
                 load_k(jn, x);
         }
         // element e of this lane: key kb + (e/4)*16 + 4*kg + e%4, column lr
-        const bool full = j < n_cache_blk && kb + kKb <= ce && (window <= 0 || kb >= P + nq - window);
+        const bool full = j < n_cache_blk && !merged && kb + kKb <= ce && (window <= 0 || kb >= P + nq - window);
         float xs[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
