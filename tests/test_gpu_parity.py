@@ -351,6 +351,19 @@ def test_verify_contig(splits, ws):
     assert_close(o, _ref_cached(layer, cl, 0), torch.bfloat16, "contig verify")
 
 
+@pytest.mark.parametrize("nq,splits", [(2, 0), (2, 3), (3, 1), (3, 0)])
+def test_verify_contig_column_counts(nq, splits):
+    """Verify of 2 and 3 tokens on a global layer (16 heads per KV head: 32 and 48
+    (token, head) columns) -- the LDS-staged verify kernel with idle waves --
+    over contexts that end on, just past and just before 32-key block edges."""
+    _print_case("verify contig columns", nq, splits)
+    cl = torch.tensor([0, 31, 32, 33, 95, 1000], dtype=torch.int32)
+    layer = _layer(101 + nq, cl, nq, 64, 4, 0, sinks=sink_for_half_mass(1000))
+    o, _, _ = _run_cached(layer, cl, ops.CONTIG, 0, 1040, 4, verify=True, num_splits=splits,
+                          ws_splits=max(splits, 8))
+    assert_close(o, _ref_cached(layer, cl, 0), torch.bfloat16, "contig verify columns")
+
+
 @pytest.mark.parametrize("nq", [1, 2, 3, 8])
 def test_verify_query_counts(nq):
     _print_case("verify nq", nq)
