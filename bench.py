@@ -404,7 +404,8 @@ def measured_peaks(torch, dev, reps=10):
     copy_gbs = 2 * src.numel() * 2 / (t.mean_ms() * 1e-3) / 1e9
     del src, dst
     # read-only streaming over a 4 GiB buffer: the calibration kernel of
-    # libsinkattn_calib.so (each 16-byte piece loaded once), best grid of four
+    # libsinkattn_calib.so (each 16-byte piece loaded once, non-temporal), best
+    # grid of four
     import ctypes
     calib = ctypes.CDLL(os.path.join(ROOT, "sliding_window_sink_amd", "libsinkattn_calib.so"))
     calib.calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
@@ -441,7 +442,8 @@ def measured_peaks(torch, dev, reps=10):
     return dict(copy_gbs=round(copy_gbs, 1), read_gbs=round(read_gbs, 1),
                 gemm_bf16_tflops=round(gemm_tflops, 1),
                 copy="1 GiB int16 torch copy_ (read + write)",
-                read="4 GiB read-only stream (calibration kernel, %d workgroups)" % read_blocks,
+                read="4 GiB read-only stream (calibration kernel: a contiguous chunk per "
+                     "workgroup, non-temporal loads, %d workgroups)" % read_blocks,
                 gemm="bf16 8192^3 torch.matmul")
 
 

@@ -45,6 +45,10 @@ constexpr uint32_t kOob = 0x80000000u;
 
 // ------------------------------------------------------------------ preprocess
 
+__device__ __forceinline__ uint4 load16_nt(const uint16_t *p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4 *)p));
+}
+
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 4, li = lane & 15;
@@ -52,8 +56,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     const int64_t n_rows = (int64_t)a.B * a.T * a.Hq;
     float d = 0.f;
     if (row < n_rows) {
-        const uint4 o = *(const uint4 *)((const uint16_t *)a.o + row * kDv + li * 8);
-        const uint4 g = *(const uint4 *)((const uint16_t *)a.dout + row * kDv + li * 8);
+        // whole rows read once (16 lanes x 16 bytes): non-temporal loads
+        const uint4 o = load16_nt((const uint16_t *)a.o + row * kDv + li * 8);
+        const uint4 g = load16_nt((const uint16_t *)a.dout + row * kDv + li * 8);
         const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {

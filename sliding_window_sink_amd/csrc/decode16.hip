@@ -193,10 +193,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             const int slot = a.ring ? p % a.cap : p;
             const uint32_t off =
                 p < ce ? ((uint32_t)slot * kDv + (uint32_t)lr * 8) * kEs : kOob;
+            // a load instruction reads whole V rows: non-temporal (read once)
             if constexpr (kFp8)
-                x.v[e] = buf_load8(vc, off);
+                x.v[e] = buf_load8_nt(vc, off);
             else
-                x.v[e] = buf_load16(vc, off);
+                x.v[e] = buf_load16_nt(vc, off);
         }
     };
     auto load_new = [&](KV16 &x) {

@@ -63,9 +63,13 @@ __device__ __forceinline__ f32x4v mfma16x16x32(const bf16x8 &a, const bf16x8 &b,
 }
 
 // One 1 KB global->LDS load: lane l's 16 bytes at r + off land at lds + 16 l.
+// kNt: the non-temporal cache policy, for the V pieces, whose load instructions
+// read whole rows once (on the K pieces, 64-byte halves of 128-byte lines, it
+// measured slower: the other half is then fetched again).
+template <bool kNt>
 __device__ __forceinline__ void lds_load16(BufRsrc r, uint8_t *lds, uint32_t off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
-                                             off, 0, 0, 0);
+                                             off, 0, 0, kNt ? kCacheNt : 0);
 }
 
 // Wait until at most N vector memory operations of this thread are outstanding
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_lds_kernel(CachedArgs a, f
             const int p = kb + 16 * kt + lr;
             const uint32_t off = ((uint32_t)p * (kDqk * 2) + (uint32_t)(32 * s + 8 * kg) * 2) |
                                  blk_oob | (p < ce ? 0u : kOob);
-            lds_load16(kc, slot + pc * 1024, off);
+            lds_load16<false>(kc, slot + pc * 1024, off);
         }
 #pragma unroll
         for (int u = 0; u < (kPieces - kKPieces) / kWaves; ++u) {
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_lds_kernel(CachedArgs a, f
             const int chunk = lr ^ (row & 15);
             const uint32_t off = ((uint32_t)p * (kDv * 2) + (uint32_t)chunk * 16) | blk_oob |
                                  (p < ce ? 0u : kOob);
-            lds_load16(vc, slot + kKBytes + pv * 1024, off);
+            lds_load16<true>(vc, slot + kKBytes + pv * 1024, off);
         }
     };
     load_block(kv0, 0);
