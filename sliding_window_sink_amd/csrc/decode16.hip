@@ -193,11 +193,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             const int slot = a.ring ? p % a.cap : p;
             const uint32_t off =
                 p < ce ? ((uint32_t)slot * kDv + (uint32_t)lr * 8) * kEs : kOob;
-            // a load instruction reads whole V rows: non-temporal (read once)
+            // a load instruction reads whole V rows: non-temporal when each row is
+            // read once (token waves read every row once per wave: keep them in L2)
             if constexpr (kFp8)
-                x.v[e] = buf_load8_nt(vc, off);
+                x.v[e] = kTok ? buf_load8(vc, off) : buf_load8_nt(vc, off);
             else
-                x.v[e] = buf_load16_nt(vc, off);
+                x.v[e] = kTok ? buf_load16(vc, off) : buf_load16_nt(vc, off);
         }
     };
     auto load_new = [&](KV16 &x) {
