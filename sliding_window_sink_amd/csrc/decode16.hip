@@ -90,10 +90,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     using KVc = typename std::conditional<kFp8, KV8, KV16>::type;  // cache block registers
     constexpr uint32_t kEs = kFp8 ? 1 : 2;  // bytes per cached element
     // kTok = false: <= 16 columns, the waves split the key blocks and merge.
-    // kTok = true: <= 64 columns, wave w owns columns 16w .. 16w+15 and reads
-    // every key block (the 4 waves stream the same rows: one HBM read, L2 hits).
-    constexpr int kMerge = kTok ? 0 : kWaves - 1;
-    __shared__ __attribute__((aligned(16))) float merge[kTok ? 1 : kMerge][kCols][kMergeStride];
+    // kTok = true: <= 64 columns in n_cg groups of 16; wave w owns column group
+    // w % n_cg and, when fewer than 4 groups leave waves over, takes every n_kh-th
+    // key block (phase w / n_cg); the phases of a group merge like the waves of
+    // the other mode (the waves stream the same rows: one HBM read, L2 hits).
+    constexpr int kMerge = kWaves - 1;  // parked states at most
+    __shared__ __attribute__((aligned(16))) float merge[kMerge][kCols][kMergeStride];
     __shared__ float2 rope_tab[(kTok ? kMaxNqTok : kMaxNq) * 32];
     __shared__ uint4 new_row[(kDqk + kDv) / 8];  // one new token's k, v rows (merged block)
     const int tid = threadIdx.x, lane = tid & 63;
@@ -132,7 +134,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
 
     // Q^T operand (B of the QK MFMA): column col = (token t, head) = divmod(col, group).
     // Issued first, rotated once the RoPE table is ready.
-    const int col = kTok ? kCols * wave + lr : lr;
+    const int n_cg = kTok ? min(kWaves, (n_cols + kCols - 1) / kCols) : 1;  // column groups
+    const int n_kh = kTok ? kWaves / n_cg : kWaves;  // key phases per column group
+    const int cw = kTok ? wave % n_cg : 0, kh = kTok ? wave / n_cg : wave;
+    const bool active = kh < n_kh;  // wave-uniform (3 column groups leave wave 3 idle)
+    const int col = kTok ? kCols * cw + lr : lr;
     const bool col_ok = col < n_cols;
     const int qpos = col_ok ? P + col / group : -1;
     uint4 qr[kDqk / 32];
@@ -234,9 +240,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     }
     KVc x;
     if constexpr (kTok) {
-        if (kCols * wave < n_cols && n_cache_blk > 0) {
-            load_k(0, x);
-            load_v(0, x);
+        if (active && kh < n_cache_blk) {
+            load_k(kh, x);
+            load_v(kh, x);
         }
     } else {
         if (wave < n_cache_blk) {
@@ -391,10 +397,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // share each SIMD (a second register set per wave measured slower: one wave
     // per SIMD).
     if constexpr (kTok) {
-        if (kCols * wave < n_cols) {  // wave-uniform: this wave owns some columns
-            for (int j = 0; j < n_cache_blk; ++j)
-                compute(j, j + 1, x);
-            if (nblk > n_cache_blk) {
+        if (active) {  // wave-uniform
+            for (int j = kh; j < n_cache_blk; j += n_kh)
+                compute(j, j + n_kh, x);
+            if (nblk > n_cache_blk && n_cache_blk % n_kh == kh) {
                 KV16 xn;
                 load_new(xn);
                 compute(n_cache_blk, nblk, xn);
@@ -414,10 +420,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     float lt = l + __shfl_xor(l, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
 
-    // merge: waves 1..3 park (acc, m, l) in LDS; wave 0 folds them in and writes.
-    // acc[db][i] holds dim 8*(4kg + i) + db of column lr.
-    if (!kTok && wave > 0 && col_ok) {
-        float *e = &merge[wave - 1][lr][0];
+    // merge: the waves of phases 1 .. n_kh-1 of a column group park (acc, m, l) in
+    // LDS (slot (phase-1) * n_cg + group); phase 0 folds them in, in phase order,
+    // and writes.  acc[db][i] holds dim 8*(4kg + i) + db of column lr.
+    const int n_park = n_kh - 1;
+    if (active && kh > 0 && col_ok) {
+        float *e = &merge[(kh - 1) * n_cg + cw][lr][0];
         if (kg == 0) {
             e[kDv] = m;
             e[kDv + 1] = lt;
@@ -429,9 +437,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             *(float4 *)&e[d0 + 4] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
         }
     }
-    if constexpr (!kTok)
+    if (n_park > 0)  // uniform
         __syncthreads();
-    if ((kTok || wave == 0) && col_ok) {
+    if (active && kh == 0 && col_ok) {
         const bool write_final = a.n_splits == 1;
         const size_t rows_total = (size_t)a.B * nq * Hq;
         const int t = col / group;
@@ -440,7 +448,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
         float mx = m;
 #pragma unroll
         for (int w = 0; w < kMerge; ++w)
-            mx = fmaxf(mx, merge[w][lr][kDv]);
+            if (w < n_park)
+                mx = fmaxf(mx, merge[w * n_cg + cw][lr][kDv]);
         float M = mx, zs = 0.f;
         if (write_final) {
             const float sink2 = a.sink[h] * kLog2e;
@@ -448,13 +457,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             zs = (sink2 == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(sink2 - M);
         }
         const float f0 = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-        float fw[kMerge > 0 ? kMerge : 1];
+        float fw[kMerge];
         float z = zs + lt * f0;
 #pragma unroll
         for (int w = 0; w < kMerge; ++w) {
-            const float mw = merge[w][lr][kDv];
-            fw[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-            z += merge[w][lr][kDv + 1] * fw[w];
+            fw[w] = 0.f;
+            if (w < n_park) {
+                const float mw = merge[w * n_cg + cw][lr][kDv];
+                fw[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+                z += merge[w * n_cg + cw][lr][kDv + 1] * fw[w];
+            }
         }
         const float so = write_final ? (z > 0.f ? 1.f / z : 0.f) : 1.f;
 #pragma unroll
@@ -466,8 +478,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
                 vals[db] = acc[db][i] * f0;
 #pragma unroll
             for (int w = 0; w < kMerge; ++w) {
-                const float4 p0 = *(const float4 *)&merge[w][lr][d0];
-                const float4 p1 = *(const float4 *)&merge[w][lr][d0 + 4];
+                if (w >= n_park)
+                    break;
+                const float4 p0 = *(const float4 *)&merge[w * n_cg + cw][lr][d0];
+                const float4 p1 = *(const float4 *)&merge[w * n_cg + cw][lr][d0 + 4];
                 vals[0] += p0.x * fw[w];
                 vals[1] += p0.y * fw[w];
                 vals[2] += p0.z * fw[w];
