@@ -15,14 +15,17 @@
 // flash-attention backward it otherwise follows.
 //
 // Kernels:
-//   bwd_pre_kernel   D and -p_i D_i per (token, head)  (one 16-lane group per row)
+//   bwd_pre_kernel   D and -p_i D_i per (token, head)  (one 16-lane group per row,
+//                    four rows per group so that eight loads are in flight)
 //   bwd_dsink_kernel dsink_h = fixed-order sum over tokens (deterministic)
 //   bwd_dq_kernel    per (KV group, head half, 32-query tile), 8 waves = 8 heads:
 //                    the forward's layout -- S^T = K Q^T with each lane owning a
 //                    query column, K rows permuted so C-register i of half hh is
 //                    key 16hh + i; dP^T = V dO^T with V rows permuted the same
 //                    way; dQ^T += K^T dS^T with the K^T operand read from the
-//                    same K rows by gfx950's transposing LDS loads.
+//                    same K rows by gfx950's transposing LDS loads.  The tile's
+//                    Q / dO rows come in and its fp32 dQ rows go out in whole
+//                    128-byte lines per instruction, regrouped through LDS.
 //   bwd_dkdv_kernel  per (KV group, 64-key block), 4 waves of 16 keys each, every
 //                    query head of the group: 16x16x32 products, S = Q K^T with
 //                    each lane owning a key column and Q rows permuted so the C
@@ -31,7 +34,11 @@
 //                    dK^T += Q^T dS; the step's Q and dO tile is shared by the
 //                    4 waves, put into LDS two steps ahead by global->LDS loads
 //                    in MFMA operand order (the Q^T / dO^T operands come from
-//                    the same pieces through transposing reads).
+//                    the same pieces through transposing reads); dK / dV rows
+//                    leave in whole 128-byte lines, regrouped through LDS.
+// Whole-line stores matter here: the fp32 gradient rows are the largest stream
+// of the SWA backward, and stores that cover a quarter of a line per instruction
+// ran the dQ kernel ~25% slower (0.99 vs 0.75 ms at T 32768, W 128).
 // Every output element is written once (no atomics): results are deterministic.
 #include "common.h"
 #include "lds_tr.h"
@@ -49,36 +56,45 @@ __device__ __forceinline__ uint4 load16_nt(const uint16_t *p) {
     return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4 *)p));
 }
 
+constexpr int kPreRows = 4;  // rows per 16-lane group (8 loads in flight per lane)
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 4, li = lane & 15;
-    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + grp;  // (b*T+t)*Hq + h
+    const int gi = (threadIdx.x >> 6) * 4 + grp;  // 16 groups; group gi takes rows gi + 16j
     const int64_t n_rows = (int64_t)a.B * a.T * a.Hq;
-    float d = 0.f;
-    if (row < n_rows) {
+    const int64_t row_base = (int64_t)blockIdx.x * 16 * kPreRows + gi;  // (b*T+t)*Hq + h
+    uint4 o[kPreRows], g[kPreRows];
+#pragma unroll
+    for (int j = 0; j < kPreRows; ++j) {
+        const int64_t row = min(row_base + 16 * j, n_rows - 1);
         // whole rows read once (16 lanes x 16 bytes): non-temporal loads
-        const uint4 o = load16_nt((const uint16_t *)a.o + row * kDv + li * 8);
-        const uint4 g = load16_nt((const uint16_t *)a.dout + row * kDv + li * 8);
-        const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
+        o[j] = load16_nt((const uint16_t *)a.o + row * kDv + li * 8);
+        g[j] = load16_nt((const uint16_t *)a.dout + row * kDv + li * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < kPreRows; ++j) {
+        const int64_t row = row_base + 16 * j;
+        float d = 0.f;
+        const uint32_t ow[4] = {o[j].x, o[j].y, o[j].z, o[j].w}, gw[4] = {g[j].x, g[j].y, g[j].z, g[j].w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float x = bf16_bits_to_f32((uint16_t)(ow[i >> 1] >> (16 * (i & 1))));
             const float y = bf16_bits_to_f32((uint16_t)(gw[i >> 1] >> (16 * (i & 1))));
             d = __fmaf_rn(x, y, d);
         }
-    }
 #pragma unroll
-    for (int o = 8; o >= 1; o >>= 1)
-        d += __shfl_xor(d, o, 64);
-    if (row < n_rows && li == 0) {
-        const int h = (int)(row % a.Hq);
-        const int64_t bt = row / a.Hq;
-        const int t = (int)(bt % a.T), b = (int)(bt / a.T);
-        const size_t idx = ((size_t)b * a.Hq + h) * a.T + t;
-        a.D[idx] = d;
-        const float lse = a.lse[idx], sink = a.sink[h];
-        const float ps = (sink == -INFINITY) ? 0.f : __expf(sink - lse);
-        a.PS[idx] = -ps * d;
+        for (int m = 8; m >= 1; m >>= 1)
+            d += __shfl_xor(d, m, 64);
+        if (row < n_rows && li == 0) {
+            const int h = (int)(row % a.Hq);
+            const int64_t bt = row / a.Hq;
+            const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+            const size_t idx = ((size_t)b * a.Hq + h) * a.T + t;
+            a.D[idx] = d;
+            const float lse = a.lse[idx], sink = a.sink[h];
+            const float ps = (sink == -INFINITY) ? 0.f : __expf(sink - lse);
+            a.PS[idx] = -ps * d;
+        }
     }
 }
 
@@ -126,6 +142,7 @@ template <bool kWindowed>
 __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_units, int n_tiles,
                                                            float scale_log2) {
     __shared__ DqSmem sm;
+    __shared__ float xch[kQWaves][kTq * 36];  // per-wave row exchange: 32 rows x (128 + 16) bytes
     const int T = a.T, Hq = a.Hq, Hkv = a.Hkv, window = a.window;
     const int group = Hq / Hkv, parts = group / kQWaves;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -150,16 +167,46 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
     const uint32_t kcol = (uint32_t)g * kDqk * 2, vcol = (uint32_t)g * kDv * 2;
 
     // B operands held for the whole tile: Q^T (k-step s: dims (2s+hh)*8 ..) and dO^T.
+    // The rows are fetched in whole 128-byte lines (8 lanes x 16 bytes of one row per
+    // line; rows 8i + lane/8 in instruction i) and regrouped into the operand layout
+    // through a per-wave LDS area, one line column (32 rows x 128 bytes) at a time.
     uint4 qf[kDqk / 16], gf[kDv / 16];
     {
-        const uint32_t qo = (uint32_t)query * qrow + (uint32_t)h * kDqk * 2 + (uint32_t)hh * 16;
-        const uint32_t go = (uint32_t)query * orow + (uint32_t)h * kDv * 2 + (uint32_t)hh * 16;
+        const int lr8 = lane >> 3, c8 = lane & 7;
+        uint4 rq[kDqk / 16], rg[kDv / 16];
 #pragma unroll
-        for (int s = 0; s < kDqk / 16; ++s)
-            qf[s] = buf_load16(qbuf, qo + (uint32_t)s * 32);
+        for (int li = 0; li < kDqk / 64; ++li)
 #pragma unroll
-        for (int s = 0; s < kDv / 16; ++s)
-            gf[s] = buf_load16(gbuf, go + (uint32_t)s * 32);
+            for (int i = 0; i < 4; ++i)
+                rq[4 * li + i] = buf_load16(qbuf, (uint32_t)(t0 + 8 * i + lr8) * qrow + (uint32_t)h * kDqk * 2 +
+                                                      128 * li + 16 * c8);
+#pragma unroll
+        for (int li = 0; li < kDv / 64; ++li)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                rg[4 * li + i] = buf_load16(gbuf, (uint32_t)(t0 + 8 * i + lr8) * orow + (uint32_t)h * kDv * 2 +
+                                                      128 * li + 16 * c8);
+        uint4 *xs = (uint4 *)xch[wave];  // row pitch 9 pieces (128 + 16 bytes)
+        auto regroup = [&](const uint4 *raw, uint4 *dst) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xs[(8 * i + lr8) * 9 + c8] = raw[i];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                dst[s4] = xs[r * 9 + 2 * s4 + hh];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        };
+#pragma unroll
+        for (int li = 0; li < kDqk / 64; ++li)
+            regroup(rq + 4 * li, qf + 4 * li);
+#pragma unroll
+        for (int li = 0; li < kDv / 64; ++li)
+            regroup(rg + 4 * li, gf + 4 * li);
     }
     const bool qok = query < T;
     const size_t lidx = ((size_t)b * Hq + h) * T + (qok ? query : 0);
@@ -258,18 +305,34 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
             load_block(kb + 2 * kKb, st);
     }
 
-    // dq[query][h][dim] = scale * acc; C row (i/4)*8 + 4hh + i%4 of tile d = dim 32d + ...
-    if (qok) {
-        float *dst = a.dq + ((row0 + query) * Hq + h) * kDqk;
+    // dq[query][h][dim] = scale * acc (C row (i/4)*8 + 4hh + i%4 of tile d = dim
+    // 32d + 8(i/4) + 4hh + i%4).  The rows leave through LDS so that every store
+    // instruction writes whole 128-byte lines: 8 lanes x 16 bytes of one
+    // (query, head) row's 32 dims of tile d.
+    {
+        float *stage = xch[wave];  // 32 rows x (32 + 4) floats
+        const int nq = min(kTq, T - t0);
+        const BufRsrc dqbuf = make_buf(a.dq + ((row0 + t0) * Hq) * kDqk, (uint64_t)nq * Hq * kDqk * 4);
 #pragma unroll
-        for (int d = 0; d < kDqk / 32; ++d)
+        for (int d = 0; d < kDqk / 32; ++d) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int dim = 32 * d + 8 * q4 + 4 * hh;
-                *(float4 *)(dst + dim) =
+            for (int q4 = 0; q4 < 4; ++q4)
+                *(float4 *)(stage + r * 36 + 8 * q4 + 4 * hh) =
                     make_float4(acc[d][4 * q4] * a.scale, acc[d][4 * q4 + 1] * a.scale,
                                 acc[d][4 * q4 + 2] * a.scale, acc[d][4 * q4 + 3] * a.scale);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int row = 8 * it + (lane >> 3), c = lane & 7;
+                const uint4 w = *(const uint4 *)(stage + row * 36 + 4 * c);
+                buf_store16(dqbuf, (uint32_t)(row * Hq + h) * (kDqk * 4) + 128 * d + 16 * c, w);
             }
+        }
     }
 }
 
@@ -528,18 +591,39 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n
         step(k + 2, st2, ls2, st1, ls1);
     }
     wait_vmem<0>();  // no load into LDS outlives the workgroup
+    wg_barrier();    // every wave is done with the slots: st0 is reused below
 
-    if (key < T) {
-        const size_t trow = (row0 + key) * Hkv + g;
+    // dK / dV rows leave through LDS, one 32-dim column (128 bytes of each key's row)
+    // at a time, so that every store instruction writes whole 128-byte lines
+    // (8 lanes x 16 bytes of one key's row; keys kw + 8it + lane/8).
+    {
+        uint8_t *xs = st0 + wave * (kKPerWave * 144);  // 16 rows x (128 + 16) bytes
+        const int nk = max(0, min(kKPerWave, T - kw));
+        const BufRsrc dkbuf = make_buf(a.dk + ((row0 + kw) * Hkv) * kDqk, (uint64_t)nk * Hkv * kDqk * 4);
+        const BufRsrc dvbuf = make_buf(a.dv + ((row0 + kw) * Hkv) * kDv, (uint64_t)nk * Hkv * kDv * 4);
+        const int lr8 = lane >> 3, c8 = lane & 7;
+        auto emit = [&](const f32x4v &x0, const f32x4v &x1, const BufRsrc &dst, uint32_t rowbytes, int c) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            *(f32x4v *)(xs + lr * 144 + 16 * lg) = x0;
+            *(f32x4v *)(xs + lr * 144 + 64 + 16 * lg) = x1;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int dt = 0; dt < kDqk / 16; ++dt) {
-            const f32x4v x = dk[dt] * a.scale;
-            *(float4 *)&a.dk[trow * kDqk + 16 * dt + 4 * lg] = make_float4(x[0], x[1], x[2], x[3]);
-        }
+            for (int it = 0; it < 2; ++it) {
+                const int row = 8 * it + lr8;
+                const uint4 w = *(const uint4 *)(xs + row * 144 + 16 * c8);
+                buf_store16(dst, (uint32_t)(row * Hkv + g) * rowbytes + 128 * c + 16 * c8, w);
+            }
+        };
 #pragma unroll
-        for (int dt = 0; dt < kDv / 16; ++dt)
-            *(float4 *)&a.dv[trow * kDv + 16 * dt + 4 * lg] =
-                make_float4(dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]);
+        for (int c = 0; c < kDqk / 32; ++c)
+            emit(dk[2 * c] * a.scale, dk[2 * c + 1] * a.scale, dkbuf, kDqk * 4, c);
+#pragma unroll
+        for (int c = 0; c < kDv / 32; ++c)
+            emit(dv[2 * c], dv[2 * c + 1], dvbuf, kDv * 4, c);
     }
 }
 
@@ -548,7 +632,7 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n
 hipError_t launch_backward(const BwdArgs &a, hipStream_t s) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const int64_t n_rows = (int64_t)a.B * a.T * a.Hq;
-    const unsigned pre_blocks = (unsigned)((n_rows + 15) / 16);
+    const unsigned pre_blocks = (unsigned)((n_rows + 16 * kPreRows - 1) / (16 * kPreRows));
     bwd_pre_kernel<<<dim3(pre_blocks), dim3(256), 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
