@@ -15,17 +15,17 @@
 // flash-attention backward it otherwise follows.
 //
 // Kernels:
-//   bwd_pre_kernel   D and -p_i D_i per (token, head)  (one 16-lane group per row,
-//                    four rows per group so that eight loads are in flight)
-//   bwd_dsink_kernel dsink_h = fixed-order sum over tokens (deterministic)
 //   bwd_dq_kernel    per (KV group, head half, 32-query tile), 8 waves = 8 heads:
-//                    the forward's layout -- S^T = K Q^T with each lane owning a
+//                    first D_i = dO_i . o_i and -p_i D_i of the tile's rows (o is
+//                    read here, beside dO, instead of in a pass of its own), then
+//                    dQ in the forward's layout -- S^T = K Q^T with each lane owning a
 //                    query column, K rows permuted so C-register i of half hh is
 //                    key 16hh + i; dP^T = V dO^T with V rows permuted the same
 //                    way; dQ^T += K^T dS^T with the K^T operand read from the
 //                    same K rows by gfx950's transposing LDS loads.  The tile's
 //                    Q / dO rows come in and its fp32 dQ rows go out in whole
 //                    128-byte lines per instruction, regrouped through LDS.
+//   bwd_dsink_kernel dsink_h = fixed-order sum over tokens (deterministic)
 //   bwd_dkdv_kernel  per (KV group, 64-key block), 4 waves of 16 keys each, every
 //                    query head of the group: 16x16x32 products, S = Q K^T with
 //                    each lane owning a key column and Q rows permuted so the C
@@ -50,52 +50,17 @@ constexpr int kKb = 32;   // keys per block
 constexpr int kTq = 32;   // queries per tile
 constexpr uint32_t kOob = 0x80000000u;
 
-// ------------------------------------------------------------------ preprocess
+// ------------------------------------------------------------------ D, dsink
 
-__device__ __forceinline__ uint4 load16_nt(const uint16_t *p) {
-    return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4 *)p));
-}
-
-constexpr int kPreRows = 4;  // rows per 16-lane group (8 loads in flight per lane)
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int grp = lane >> 4, li = lane & 15;
-    const int gi = (threadIdx.x >> 6) * 4 + grp;  // 16 groups; group gi takes rows gi + 16j
-    const int64_t n_rows = (int64_t)a.B * a.T * a.Hq;
-    const int64_t row_base = (int64_t)blockIdx.x * 16 * kPreRows + gi;  // (b*T+t)*Hq + h
-    uint4 o[kPreRows], g[kPreRows];
+// sum over the 8 bf16 pairs of two 16-byte chunks, in element order (fma chain)
+__device__ __forceinline__ float dot8_bf16(const uint4 &x, const uint4 &y) {
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, yw[4] = {y.x, y.y, y.z, y.w};
+    float d = 0.f;
 #pragma unroll
-    for (int j = 0; j < kPreRows; ++j) {
-        const int64_t row = min(row_base + 16 * j, n_rows - 1);
-        // whole rows read once (16 lanes x 16 bytes): non-temporal loads
-        o[j] = load16_nt((const uint16_t *)a.o + row * kDv + li * 8);
-        g[j] = load16_nt((const uint16_t *)a.dout + row * kDv + li * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < kPreRows; ++j) {
-        const int64_t row = row_base + 16 * j;
-        float d = 0.f;
-        const uint32_t ow[4] = {o[j].x, o[j].y, o[j].z, o[j].w}, gw[4] = {g[j].x, g[j].y, g[j].z, g[j].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float x = bf16_bits_to_f32((uint16_t)(ow[i >> 1] >> (16 * (i & 1))));
-            const float y = bf16_bits_to_f32((uint16_t)(gw[i >> 1] >> (16 * (i & 1))));
-            d = __fmaf_rn(x, y, d);
-        }
-#pragma unroll
-        for (int m = 8; m >= 1; m >>= 1)
-            d += __shfl_xor(d, m, 64);
-        if (row < n_rows && li == 0) {
-            const int h = (int)(row % a.Hq);
-            const int64_t bt = row / a.Hq;
-            const int t = (int)(bt % a.T), b = (int)(bt / a.T);
-            const size_t idx = ((size_t)b * a.Hq + h) * a.T + t;
-            a.D[idx] = d;
-            const float lse = a.lse[idx], sink = a.sink[h];
-            const float ps = (sink == -INFINITY) ? 0.f : __expf(sink - lse);
-            a.PS[idx] = -ps * d;
-        }
-    }
+    for (int i = 0; i < 8; ++i)
+        d = __fmaf_rn(bf16_bits_to_f32((uint16_t)(xw[i >> 1] >> (16 * (i & 1)))),
+                      bf16_bits_to_f32((uint16_t)(yw[i >> 1] >> (16 * (i & 1)))), d);
+    return d;
 }
 
 // dsink_h = sum over (b, t) of PS[b][h][t]: one workgroup per head, fixed order.
@@ -162,6 +127,7 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
     const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
     const BufRsrc qbuf = make_buf((const uint16_t *)a.q + row0 * Hq * kDqk, (uint64_t)T * qrow);
     const BufRsrc gbuf = make_buf((const uint16_t *)a.dout + row0 * Hq * kDv, (uint64_t)T * orow);
+    const BufRsrc obuf = make_buf((const uint16_t *)a.o + row0 * Hq * kDv, (uint64_t)T * orow);
     const BufRsrc kbuf = make_buf((const uint16_t *)a.k + row0 * Hkv * kDqk, (uint64_t)T * krow);
     const BufRsrc vbuf = make_buf((const uint16_t *)a.v + row0 * Hkv * kDv, (uint64_t)T * vrow);
     const uint32_t kcol = (uint32_t)g * kDqk * 2, vcol = (uint32_t)g * kDv * 2;
@@ -173,7 +139,7 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
     uint4 qf[kDqk / 16], gf[kDv / 16];
     {
         const int lr8 = lane >> 3, c8 = lane & 7;
-        uint4 rq[kDqk / 16], rg[kDv / 16];
+        uint4 rq[kDqk / 16], rg[kDv / 16], ro[kDv / 16];
 #pragma unroll
         for (int li = 0; li < kDqk / 64; ++li)
 #pragma unroll
@@ -185,6 +151,12 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 rg[4 * li + i] = buf_load16(gbuf, (uint32_t)(t0 + 8 * i + lr8) * orow + (uint32_t)h * kDv * 2 +
+                                                      128 * li + 16 * c8);
+#pragma unroll
+        for (int li = 0; li < kDv / 64; ++li)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ro[4 * li + i] = buf_load16(obuf, (uint32_t)(t0 + 8 * i + lr8) * orow + (uint32_t)h * kDv * 2 +
                                                       128 * li + 16 * c8);
         uint4 *xs = (uint4 *)xch[wave];  // row pitch 9 pieces (128 + 16 bytes)
         auto regroup = [&](const uint4 *raw, uint4 *dst) {
@@ -207,11 +179,32 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
 #pragma unroll
         for (int li = 0; li < kDv / 64; ++li)
             regroup(rg + 4 * li, gf + 4 * li);
+        // D of rows 8i + lane/8: 8-dim partial dot products, the two line columns
+        // added, then summed over the row's 8 lanes
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float d = dot8_bf16(ro[i], rg[i]) + dot8_bf16(ro[4 + i], rg[4 + i]);
+#pragma unroll
+            for (int m = 4; m >= 1; m >>= 1)
+                d += __shfl_xor(d, m, 64);
+            if (c8 == 0)
+                xch[wave][8 * i + lr8] = d;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     const bool qok = query < T;
     const size_t lidx = ((size_t)b * Hq + h) * T + (qok ? query : 0);
-    const float lse2 = qok ? a.lse[lidx] * kLog2e : 0.f;
-    const float Dq = qok ? a.D[lidx] : 0.f;
+    const float lse = qok ? a.lse[lidx] : 0.f;
+    const float lse2 = lse * kLog2e;
+    const float Dq = qok ? xch[wave][r] : 0.f;
+    if (qok && hh == 0) {
+        a.D[lidx] = Dq;
+        const float sink = a.sink[h];
+        const float ps = (sink == -INFINITY) ? 0.f : __expf(sink - lse);
+        a.PS[lidx] = -ps * Dq;
+    }
 
     const int kstart = kWindowed ? max(0, t0 - window + 1) : 0;
     const int kend = min(T, t0 + kTq);
@@ -631,15 +624,7 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n
 
 hipError_t launch_backward(const BwdArgs &a, hipStream_t s) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    const int64_t n_rows = (int64_t)a.B * a.T * a.Hq;
-    const unsigned pre_blocks = (unsigned)((n_rows + 16 * kPreRows - 1) / (16 * kPreRows));
-    bwd_pre_kernel<<<dim3(pre_blocks), dim3(256), 0, s>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    bwd_dsink_kernel<<<dim3((unsigned)a.Hq), dim3(kSinkThreads), 0, s>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
+    hipError_t e;
     const int group = a.Hq / a.Hkv;
     const int parts = group / kQWaves;
     const int q_units = a.B * a.Hkv * parts;
@@ -649,6 +634,9 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t s) {
         bwd_dq_kernel<true><<<qgrid, dim3(kQThreads), 0, s>>>(a, q_units, n_tiles, scale_log2);
     else
         bwd_dq_kernel<false><<<qgrid, dim3(kQThreads), 0, s>>>(a, q_units, n_tiles, scale_log2);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    bwd_dsink_kernel<<<dim3((unsigned)a.Hq), dim3(kSinkThreads), 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int k_units = a.B * a.Hkv;
