@@ -26,7 +26,7 @@
 //                    Q / dO rows come in and its fp32 dQ rows go out in whole
 //                    128-byte lines per instruction, regrouped through LDS.
 //   bwd_dsink_kernel dsink_h = fixed-order sum over tokens (deterministic)
-//   bwd_dkdv_kernel  per (KV group, 64-key block), 4 waves of 16 keys each, every
+//   bwd_dkdv_kernel  (windowed layers) per (KV group, 64-key block), 4 waves of 16 keys each, every
 //                    query head of the group: 16x16x32 products, S = Q K^T with
 //                    each lane owning a key column and Q rows permuted so the C
 //                    registers of a lane hold 8 consecutive queries, so P and dS
@@ -36,6 +36,9 @@
 //                    in MFMA operand order (the Q^T / dO^T operands come from
 //                    the same pieces through transposing reads); dK / dV rows
 //                    leave in whole 128-byte lines, regrouped through LDS.
+//   bwd_dkdv32_kernel (global layers) the same with 32x32x16 products: per (KV
+//                    group, 128-key block), 4 waves of 32 keys each, one wave per
+//                    SIMD; every LDS operand read feeds twice the pairs.
 // Whole-line stores matter here: the fp32 gradient rows are the largest stream
 // of the SWA backward, and stores that cover a quarter of a line per instruction
 // ran the dQ kernel ~25% slower (0.99 vs 0.75 ms at T 32768, W 128).
@@ -620,6 +623,287 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n
     }
 }
 
+// ------------------------------------------------------------------ dK, dV (global layers)
+
+// dK, dV of one 128-key block of KV group g for global (unwindowed) layers, with
+// 32x32x16 products.  Wave w owns keys kb + 32w .. +31 and keeps their dK^T / dV^T
+// (160 accumulators per lane) over every (query head, 32-query tile) step at or
+// after the block; one wave per SIMD.  Against the 16-key kernel above, every
+// operand read from LDS feeds twice the pairs (32 keys), and the 32x32x16 product
+// issues ~20% more FLOP per cycle than 16x16x32 (measured on the GPU: 2.33 vs
+// 1.94 PFLOP/s): at 16x16x32 with one LDS operand per product the products
+// would need ~120 TB/s of LDS reads against ~107 TB/s that conflict-free
+// 16-byte reads deliver.  Lane l: col = l % 32 (key), hh = l / 32.
+//   Tile layout: the step's Q rows and dO rows in query order with row pitches of
+//   400 and 304 bytes (100 and 76 dwords: 36 and 12 modulo the 64 banks), so the
+//   16-byte operand reads of S = Q K^T and dP = dO V^T (16 consecutive rows per
+//   bank pass) and the transposing reads of the Q^T / dO^T operands (4 rows x 16
+//   dims per 16 lanes) are free of bank conflicts, and every operand address is
+//   one per-lane base plus an immediate offset.  S and dP come out with C rows 8a + 4hh + e = query
+//   q0 + 8a + 4hh + e of key col; their elements 8ks .. 8ks+7 are directly the B
+//   operand (k = queries 16ks + 8t + 4hh + e, element 4t + e) of k-step ks of
+//   dV^T += dO^T P and dK^T += Q^T dS, whose A operands the transposing reads
+//   take in the same query order.
+//   K and V of the wave's 32 keys stay in registers as the B operands of S and dP.
+// The global->LDS loads of a step (six 1 KB pieces per thread, plus the tile's
+// lse and D), the three slots and the barrier follow the 16-key kernel.
+constexpr int kK32Waves = 4;
+constexpr int kK32Threads = kK32Waves * 64;
+constexpr int kK32PerWave = 32;
+constexpr int kK32Blk = kK32Waves * kK32PerWave;  // 128 keys per workgroup
+constexpr int kK32QPitch = kDqk * 2 + 16;  // 400 bytes: 24 data chunks + 1 pad
+constexpr int kK32GPitch = kDv * 2 + 48;   // 304 bytes: 16 data chunks + 3 pad
+constexpr int kK32QPieces = (kTq * kK32QPitch + 1023) / 1024;  // 13 pieces of 1 KB
+constexpr int kK32GPieces = (kTq * kK32GPitch + 1023) / 1024;  // 10
+constexpr int kK32Pieces = 24;  // 13 + 10 + 1 that loads nothing: 6 per thread
+constexpr int kK32StepBytes = kK32Pieces * 1024;
+constexpr int kK32QBytes = kK32QPieces * 1024;
+constexpr int kK32StepLoads = kK32Pieces / kK32Waves + 2;  // 8
+static_assert(kK32QPieces + kK32GPieces < kK32Pieces && kK32Pieces % kK32Waves == 0, "uniform pieces");
+
+__global__ __launch_bounds__(kK32Threads, 1) void bwd_dkdv32_kernel(BwdArgs a, int n_units, int n_blk,
+                                                                   float scale_log2) {
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[kK32StepBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[kK32StepBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[kK32StepBytes];
+    __shared__ __attribute__((aligned(16))) float ls0[kK32Waves][128];
+    __shared__ __attribute__((aligned(16))) float ls1[kK32Waves][128];
+    __shared__ __attribute__((aligned(16))) float ls2[kK32Waves][128];
+    const int T = a.T, Hq = a.Hq, Hkv = a.Hkv;
+    const int group = Hq / Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, hh = lane >> 5;
+    const int unit = blockIdx.x % n_units;
+    const int blk = blockIdx.x / n_units;  // ascending: key block 0 sees the most queries
+    const int g = unit % Hkv, b = unit / Hkv;
+    const int kb = blk * kK32Blk;
+    const int kw = kb + kK32PerWave * wave;  // this wave's first key
+    const int key = kw + col;                // this lane's key column
+    if (kb >= T)
+        return;  // uniform
+
+    const int n_tiles = (T - 1 - kb) / kTq + 1;  // queries kb .. T-1
+    const int n_steps = group * n_tiles;         // step = (head of the group, query tile)
+
+    const size_t row0 = (size_t)b * T;
+    const uint32_t qrow = (uint32_t)Hq * kDqk * 2, orow = (uint32_t)Hq * kDv * 2;
+    const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
+    const BufRsrc qbuf = make_buf((const uint16_t *)a.q + row0 * Hq * kDqk, (uint64_t)T * qrow);
+    const BufRsrc gbuf = make_buf((const uint16_t *)a.dout + row0 * Hq * kDv, (uint64_t)T * orow);
+    const BufRsrc lbuf = make_buf(a.lse + (size_t)b * Hq * T, (uint64_t)Hq * T * 4);
+    const BufRsrc dbuf = make_buf(a.D + (size_t)b * Hq * T, (uint64_t)Hq * T * 4);
+
+    // B operands: K (k-step s: dims 16s + 8hh .. +7 of key col) and V
+    uint4 kr[kDqk / 16], vr[kDv / 16];
+    {
+        const BufRsrc kbuf = make_buf((const uint16_t *)a.k + row0 * Hkv * kDqk, (uint64_t)T * krow);
+        const BufRsrc vbuf = make_buf((const uint16_t *)a.v + row0 * Hkv * kDv, (uint64_t)T * vrow);
+        const uint32_t ko = key < T ? (uint32_t)key * krow + (uint32_t)g * kDqk * 2 + (uint32_t)hh * 16 : kOob;
+        const uint32_t vo = key < T ? (uint32_t)key * vrow + (uint32_t)g * kDv * 2 + (uint32_t)hh * 16 : kOob;
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s)
+            kr[s] = buf_load16(kbuf, ko + (uint32_t)s * 32);
+#pragma unroll
+        for (int s = 0; s < kDv / 16; ++s)
+            vr[s] = buf_load16(vbuf, vo + (uint32_t)s * 32);
+    }
+
+    // Step k -> (query head, first query of the tile): tiles descending from the last
+    // one, heads inner (every block of the group walks the same sequence from the top).
+    auto step_head = [&](int k) { return g * group + k % group; };
+    auto step_q0 = [&](int k) { return kb + (n_tiles - 1 - k / group) * kTq; };
+    // This thread's 7 loads of step k into a slot: pieces wave + 4u (u < 5) of the
+    // 20 KB tile (pieces 0..11 Q rows, 12..19 dO rows), then lse and D.  Offsets with
+    // bit 31 set read nothing; every real offset is below 2^31.
+    // Piece pc = wave + 4u of a slot: 16-byte chunk 64 pc' + lane of the padded Q rows
+    // (pc' = pc < 13) or dO rows (pc' = pc - 13 < 10); chunks in the padding, past row
+    // 31 or in the last piece read nothing.  Per thread: row r_u, byte column cb_u.
+    int ld_row[kK32Pieces / kK32Waves];
+    uint32_t ld_col[kK32Pieces / kK32Waves];
+#pragma unroll
+    for (int u = 0; u < kK32Pieces / kK32Waves; ++u) {
+        const int pc = wave + kK32Waves * u;
+        if (pc < kK32QPieces) {
+            const int ci = 64 * pc + lane, r = ci / (kK32QPitch / 16), c = ci % (kK32QPitch / 16);
+            const bool ok = r < kTq && c < kDqk / 8;
+            ld_row[u] = ok ? r : 0;
+            ld_col[u] = ok ? (uint32_t)c * 16 : kOob;
+        } else if (pc < kK32QPieces + kK32GPieces) {
+            const int ci = 64 * (pc - kK32QPieces) + lane, r = ci / (kK32GPitch / 16), c = ci % (kK32GPitch / 16);
+            const bool ok = r < kTq && c < kDv / 8;
+            ld_row[u] = ok ? r : 0;
+            ld_col[u] = ok ? (uint32_t)c * 16 : kOob;
+        } else {
+            ld_row[u] = 0;
+            ld_col[u] = kOob;
+        }
+    }
+    auto load_step = [&](uint8_t *slot, int k) {
+        const uint32_t step_oob = k < n_steps ? 0u : kOob;
+        const int kk = k < n_steps ? k : 0;
+        const int h = step_head(kk);
+        const int q0 = step_q0(kk);
+#pragma unroll
+        for (int u = 0; u < kK32Pieces / kK32Waves; ++u) {
+            const int pc = wave + kK32Waves * u;
+            const int q = q0 + ld_row[u];
+            const uint32_t oob = step_oob | (q < T ? 0u : kOob);
+            // pc < 13: Q rows; else dO rows (the last piece reads nothing either way)
+            const bool isq = pc < kK32QPieces;  // wave-uniform
+            const uint32_t off = isq ? (uint32_t)q * qrow + (uint32_t)h * kDqk * 2
+                                     : (uint32_t)q * orow + (uint32_t)h * kDv * 2;
+            lds_load16(isq ? qbuf : gbuf, slot + pc * 1024, (off + ld_col[u]) | oob);
+        }
+    };
+    auto load_ld = [&](float (*ls)[128], int k) {
+        const uint32_t step_oob = k < n_steps ? 0u : kOob;
+        const int kk = k < n_steps ? k : 0;
+        const int h = step_head(kk);
+        const int q = step_q0(kk) + lane;  // lanes 0..31: the tile's queries
+        const uint32_t off = ((uint32_t)h * T + (uint32_t)q) * 4 | step_oob |
+                             (lane < kTq && q < T ? 0u : kOob);
+        lds_load4(lbuf, (uint8_t *)ls[wave], off);
+        lds_load4(dbuf, (uint8_t *)&ls[wave][64], off);
+    };
+
+    f32x16 dk[kDqk / 32], dv[kDv / 32];  // C tiles: rows dims 32dt + 8a + 4hh + e, column key col
+#pragma unroll
+    for (int d = 0; d < kDqk / 32; ++d)
+        dk[d] = f32x16{};
+#pragma unroll
+    for (int d = 0; d < kDv / 32; ++d)
+        dv[d] = f32x16{};
+
+    // Transposing-read sources of this lane (lane i = 4e + m of its 16-lane group G):
+    // query row 16ks + 8t + 4hh + e, dims 32dt + 16(G%2) + 4m .. +3.
+    const int tr_row = 4 * hh + ((lane & 15) >> 2), tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int q_tr_base = tr_row * kK32QPitch + 2 * tr_dim, g_tr_base = tr_row * kK32GPitch + 2 * tr_dim;
+    const int q_rd_base = col * kK32QPitch + 16 * hh, g_rd_base = col * kK32GPitch + 16 * hh;
+    auto q_tr = [&](const uint8_t *qs, int dt, int ks, int t) {
+        return lds_tr16((const uint16_t *)(qs + q_tr_base + (16 * ks + 8 * t) * kK32QPitch + 64 * dt));
+    };
+    auto g_tr = [&](const uint8_t *gs, int dt, int ks, int t) {
+        return lds_tr16((const uint16_t *)(gs + g_tr_base + (16 * ks + 8 * t) * kK32GPitch + 64 * dt));
+    };
+
+    auto compute = [&](const uint8_t *slot, const float (*ls)[128], int k) {
+        const int q0 = step_q0(k);
+        if (q0 + kTq - 1 < kw)
+            return;  // wave-uniform: every query of the tile precedes this wave's keys
+        const uint8_t *qs = slot, *gs = slot + kK32QBytes;
+        // A operands of S and dP: row = query col, k-step s: dims 16s + 8hh .. +7
+        uint4 qa[kDqk / 16], ga[kDv / 16];
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s) {
+            qa[s] = *(const uint4 *)(qs + q_rd_base + 32 * s);
+            if (s < kDv / 16)
+                ga[s] = *(const uint4 *)(gs + g_rd_base + 32 * s);
+        }
+        f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int s = 0; s < kDqk / 16; ++s) {
+            sc = mfma32x32x16(as_bf16x8(qa[s]), as_bf16x8(kr[s]), sc);
+            if (s < kDv / 16)
+                dp = mfma32x32x16(as_bf16x8(ga[s]), as_bf16x8(vr[s]), dp);
+        }
+        // P and dS: C register i = 4a + e holds query q0 + 8a + 4hh + e
+        const float *ld = ls[wave];
+        float lw[16], dw[16];
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa) {
+            const float4 l4 = *(const float4 *)(ld + 8 * aa + 4 * hh);
+            const float4 d4 = *(const float4 *)(ld + 64 + 8 * aa + 4 * hh);
+            lw[4 * aa] = l4.x; lw[4 * aa + 1] = l4.y; lw[4 * aa + 2] = l4.z; lw[4 * aa + 3] = l4.w;
+            dw[4 * aa] = d4.x; dw[4 * aa + 1] = d4.y; dw[4 * aa + 2] = d4.z; dw[4 * aa + 3] = d4.w;
+        }
+        // only tiles on the diagonal or past the end need the mask (uniform test)
+        if (!(q0 >= kw + kK32PerWave - 1 && q0 + kTq - 1 < T)) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int q = q0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+                sc[i] = (q < T && key <= q) ? sc[i] : -INFINITY;
+            }
+        }
+        bf16x8 pb[2], sb[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = fast_exp2(__fmaf_rn(sc[i], scale_log2, -lw[i] * kLog2e));
+            pb[i >> 3][i & 7] = (__bf16)p;
+            sb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dw[i]));
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS: k-step ks = queries 16ks .. 16ks+15
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int dt = 0; dt < kDv / 32; ++dt) {
+                const uint2 x0 = g_tr(gs, dt, ks, 0), x1 = g_tr(gs, dt, ks, 1);
+                dv[dt] = mfma32x32x16(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), pb[ks], dv[dt]);
+            }
+#pragma unroll
+            for (int dt = 0; dt < kDqk / 32; ++dt) {
+                const uint2 x0 = q_tr(qs, dt, ks, 0), x1 = q_tr(qs, dt, ks, 1);
+                dk[dt] = mfma32x32x16(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), sb[ks], dk[dt]);
+            }
+        }
+    };
+
+    load_step(st0, 0);
+    load_ld(ls0, 0);
+    load_step(st1, 1);
+    load_ld(ls1, 1);
+    auto step = [&](int k, const uint8_t *cur, const float (*lcur)[128], uint8_t *next2,
+                    float (*lnext2)[128]) {
+        wait_vmem<kK32StepLoads>();
+        wg_barrier();
+        load_step(next2, k + 2);
+        load_ld(lnext2, k + 2);
+        if (k < n_steps)
+            compute(cur, lcur, k);
+    };
+    for (int k = 0; k < n_steps; k += 3) {
+        step(k, st0, ls0, st2, ls2);
+        step(k + 1, st1, ls1, st0, ls0);
+        step(k + 2, st2, ls2, st1, ls1);
+    }
+    wait_vmem<0>();  // no load into LDS outlives the workgroup
+    wg_barrier();    // every wave is done with the slots: st0 is reused below
+
+    // dK / dV rows leave through LDS, one 32-dim tile (128 bytes of each key's row) at
+    // a time: every store instruction writes whole 128-byte lines (keys kw + 8it + lane/8).
+    {
+        uint8_t *xs = st0 + wave * (kK32PerWave * 144);  // 32 rows x (128 + 16) bytes
+        const int nk = max(0, min(kK32PerWave, T - kw));
+        const BufRsrc dkbuf = make_buf(a.dk + ((row0 + kw) * Hkv) * kDqk, (uint64_t)nk * Hkv * kDqk * 4);
+        const BufRsrc dvbuf = make_buf(a.dv + ((row0 + kw) * Hkv) * kDv, (uint64_t)nk * Hkv * kDv * 4);
+        const int lr8 = lane >> 3, c8 = lane & 7;
+        auto emit = [&](const f32x16 &x, float mul, const BufRsrc &dst, uint32_t rowbytes, int dt) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int aa = 0; aa < 4; ++aa)
+                *(float4 *)(xs + col * 144 + 32 * aa + 16 * hh) =
+                    make_float4(x[4 * aa] * mul, x[4 * aa + 1] * mul, x[4 * aa + 2] * mul, x[4 * aa + 3] * mul);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int row = 8 * it + lr8;
+                const uint4 w = *(const uint4 *)(xs + row * 144 + 16 * c8);
+                buf_store16(dst, (uint32_t)(row * Hkv + g) * rowbytes + 128 * dt + 16 * c8, w);
+            }
+        };
+#pragma unroll
+        for (int dt = 0; dt < kDqk / 32; ++dt)
+            emit(dk[dt], a.scale, dkbuf, kDqk * 4, dt);
+#pragma unroll
+        for (int dt = 0; dt < kDv / 32; ++dt)
+            emit(dv[dt], 1.f, dvbuf, kDv * 4, dt);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_backward(const BwdArgs &a, hipStream_t s) {
@@ -640,12 +924,15 @@ hipError_t launch_backward(const BwdArgs &a, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int k_units = a.B * a.Hkv;
-    const int n_blk = (a.T + kKBlk - 1) / kKBlk;
-    const dim3 kgrid((unsigned)(k_units * n_blk));
-    if (a.window > 0)
-        bwd_dkdv_kernel<true><<<kgrid, dim3(kKThreads), 0, s>>>(a, k_units, n_blk, scale_log2);
-    else
-        bwd_dkdv_kernel<false><<<kgrid, dim3(kKThreads), 0, s>>>(a, k_units, n_blk, scale_log2);
+    if (a.window > 0) {
+        const int n_blk = (a.T + kKBlk - 1) / kKBlk;
+        bwd_dkdv_kernel<true><<<dim3((unsigned)(k_units * n_blk)), dim3(kKThreads), 0, s>>>(
+            a, k_units, n_blk, scale_log2);
+    } else {
+        const int n_blk = (a.T + kK32Blk - 1) / kK32Blk;
+        bwd_dkdv32_kernel<<<dim3((unsigned)(k_units * n_blk)), dim3(kK32Threads), 0, s>>>(
+            a, k_units, n_blk, scale_log2);
+    }
     return hipGetLastError();
 }
 
