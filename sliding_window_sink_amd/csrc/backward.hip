@@ -630,16 +630,18 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n
 // (160 accumulators per lane) over every (query head, 32-query tile) step at or
 // after the block; one wave per SIMD.  Against the 16-key kernel above, every
 // operand read from LDS feeds twice the pairs (32 keys), and the 32x32x16 product
-// issues ~20% more FLOP per cycle than 16x16x32 (measured on the GPU: 2.33 vs
-// 1.94 PFLOP/s): at 16x16x32 with one LDS operand per product the products
-// would need ~120 TB/s of LDS reads against ~107 TB/s that conflict-free
-// 16-byte reads deliver.  Lane l: col = l % 32 (key), hh = l / 32.
+// issues ~20% more FLOP per cycle than 16x16x32 (2.33 vs 1.94 PFLOP/s in a
+// throughput probe on MI355X): at 16x16x32 with one LDS operand per product the
+// products would need ~120 TB/s of LDS reads against the ~107 TB/s that
+// conflict-free 16-byte reads deliver.  Lane l: col = l % 32 (key), hh = l / 32.
 //   Tile layout: the step's Q rows and dO rows in query order with row pitches of
 //   400 and 304 bytes (100 and 76 dwords: 36 and 12 modulo the 64 banks), so the
 //   16-byte operand reads of S = Q K^T and dP = dO V^T (16 consecutive rows per
 //   bank pass) and the transposing reads of the Q^T / dO^T operands (4 rows x 16
 //   dims per 16 lanes) are free of bank conflicts, and every operand address is
-//   one per-lane base plus an immediate offset.  S and dP come out with C rows 8a + 4hh + e = query
+//   one per-lane base plus an immediate offset (XOR-swizzled rows instead made
+//   the compiler's wait counts lose track of which slot a read touches).  S and
+//   dP come out with C rows 8a + 4hh + e = query
 //   q0 + 8a + 4hh + e of key col; their elements 8ks .. 8ks+7 are directly the B
 //   operand (k = queries 16ks + 8t + 4hh + e, element 4t + e) of k-step ks of
 //   dV^T += dO^T P and dK^T += Q^T dS, whose A operands the transposing reads
