@@ -54,6 +54,9 @@ def _forward(q, k, v, sink, window):
     (1, 300, 16, 2, 128),
     (1, 150, 32, 2, 0),     # global, 16 heads per KV head (two dq workgroups)
     (2, 333, 16, 1, 0),     # global, three 128-key dK/dV blocks, ragged last block
+    (3, 1, 8, 1, 0),        # global, one token: every tile and block ragged
+    (1, 31, 8, 1, 128),     # windowed, one partial tile
+    (1, 129, 64, 4, 0),     # global at the bench's head shape, one key past a block
     (1, 700, 8, 1, 512),    # W = 512 (the report's Table 2 ablation width)
 ])
 def test_backward_vs_oracle(B, T, Hq, Hkv, window):
