@@ -276,13 +276,23 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
             const bf16x8 va = as_bf16x8(*(const uint4 *)(vs + r * kVPitch + (2 * s + hh) * 8));
             dp = mfma32x32x16(va, as_bf16x8(gf[s]), dp);
         }
-        // register i holds key kb + 16hh + i of query column `query`
+        // register i holds key kb + 16hh + i of query column `query`.  Only blocks on
+        // the diagonal or the window edge need the mask (a uniform test); masked
+        // scores become -inf, so P = 0 there without a branch per element.  Query
+        // columns past the end need none: their q and dO rows, lse and D are zero,
+        // so their dS is zero.
+        const bool full = (kb + kKb - 1 <= t0) && (!kWindowed || t0 + kTq - 1 - kb < window);
+        if (!full) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = kb + 16 * hh + i;
+                sc[i] = (key <= query && (!kWindowed || query - key < window)) ? sc[i] : -INFINITY;
+            }
+        }
         bf16x8 db_[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int key = kb + 16 * hh + i;
-            const bool vis = qok && key <= query && (!kWindowed || query - key < window);
-            const float p = vis ? fast_exp2(__fmaf_rn(sc[i], scale_log2, -lse2)) : 0.f;
+            const float p = fast_exp2(__fmaf_rn(sc[i], scale_log2, -lse2));
             db_[i >> 3][i & 7] = (__bf16)(p * (dp[i] - Dq));
         }
         // dQ^T += K^T dS^T: A = K^T rows (dims), keys 16hh + 8t .. +7 of step t
