@@ -66,16 +66,20 @@ __device__ __forceinline__ float dot8_bf16(const uint4 &x, const uint4 &y) {
     return d;
 }
 
-// dsink_h = sum over (b, t) of PS[b][h][t]: one workgroup per head, fixed order.
+// dsink_h = -sum over (b, t) of e^(sink_h - lse) D: one workgroup per head, fixed
+// order (D from the workspace the dQ kernel filled).
 constexpr int kSinkThreads = 1024;
 __global__ __launch_bounds__(kSinkThreads) void bwd_dsink_kernel(BwdArgs a) {
     __shared__ float red[kSinkThreads];
     const int h = blockIdx.x;
+    const float sink = a.sink[h];
     float s = 0.f;
-    for (int b = 0; b < a.B; ++b) {
-        const float *p = a.PS + ((size_t)b * a.Hq + h) * a.T;
-        for (int t = threadIdx.x; t < a.T; t += kSinkThreads)
-            s += p[t];
+    if (sink != -INFINITY) {
+        for (int b = 0; b < a.B; ++b) {
+            const size_t row = ((size_t)b * a.Hq + h) * a.T;
+            for (int t = threadIdx.x; t < a.T; t += kSinkThreads)
+                s += -__expf(sink - a.lse[row + t]) * a.D[row + t];
+        }
     }
     red[threadIdx.x] = s;
     __syncthreads();
@@ -202,11 +206,9 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_kernel(BwdArgs a, int n_unit
     const float lse = qok ? a.lse[lidx] : 0.f;
     const float lse2 = lse * kLog2e;
     const float Dq = qok ? xch[wave][r] : 0.f;
-    if (qok && hh == 0) {
+    if (qok && hh == 0) {  // D and lse in log2 units for the dK/dV kernels
         a.D[lidx] = Dq;
-        const float sink = a.sink[h];
-        const float ps = (sink == -INFINITY) ? 0.f : __expf(sink - lse);
-        a.PS[lidx] = -ps * Dq;
+        a.L2[lidx] = lse2;
     }
 
     const int kstart = kWindowed ? max(0, t0 - window + 1) : 0;
@@ -439,7 +441,7 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n
     const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
     const BufRsrc qbuf = make_buf((const uint16_t *)a.q + row0 * Hq * kDqk, (uint64_t)T * qrow);
     const BufRsrc gbuf = make_buf((const uint16_t *)a.dout + row0 * Hq * kDv, (uint64_t)T * orow);
-    const BufRsrc lbuf = make_buf(a.lse + (size_t)b * Hq * T, (uint64_t)Hq * T * 4);
+    const BufRsrc lbuf = make_buf(a.L2 + (size_t)b * Hq * T, (uint64_t)Hq * T * 4);
     const BufRsrc dbuf = make_buf(a.D + (size_t)b * Hq * T, (uint64_t)Hq * T * 4);
 
     // B operands: K (k-step s: dims 32s + 8lg .. +7 of key lr) and V, for the whole kernel
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(kKThreads, 2) void bwd_dkdv_kernel(BwdArgs a, int n
             const int q = q0 + 8 * lg + j;
             const bool vis = q < T && key <= q && (!kWindowed || q - key < window);
             const float sv = sc[j >> 2][j & 3], dpv = dp[j >> 2][j & 3];
-            const float p = vis ? fast_exp2(__fmaf_rn(sv, scale_log2, -lw[j] * kLog2e)) : 0.f;
+            const float p = vis ? fast_exp2(__fmaf_rn(sv, scale_log2, -lw[j])) : 0.f;
             pb[j] = (__bf16)p;
             sb[j] = (__bf16)(p * (dpv - dw[j]));
         }
@@ -703,7 +705,7 @@ __global__ __launch_bounds__(kK32Threads, 1) void bwd_dkdv32_kernel(BwdArgs a, i
     const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
     const BufRsrc qbuf = make_buf((const uint16_t *)a.q + row0 * Hq * kDqk, (uint64_t)T * qrow);
     const BufRsrc gbuf = make_buf((const uint16_t *)a.dout + row0 * Hq * kDv, (uint64_t)T * orow);
-    const BufRsrc lbuf = make_buf(a.lse + (size_t)b * Hq * T, (uint64_t)Hq * T * 4);
+    const BufRsrc lbuf = make_buf(a.L2 + (size_t)b * Hq * T, (uint64_t)Hq * T * 4);
     const BufRsrc dbuf = make_buf(a.D + (size_t)b * Hq * T, (uint64_t)Hq * T * 4);
 
     // B operands: K (k-step s: dims 16s + 8hh .. +7 of key col) and V
@@ -840,7 +842,7 @@ __global__ __launch_bounds__(kK32Threads, 1) void bwd_dkdv32_kernel(BwdArgs a, i
         bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(__fmaf_rn(sc[i], scale_log2, -lw[i] * kLog2e));
+            const float p = fast_exp2(__fmaf_rn(sc[i], scale_log2, -lw[i]));
             pb[i >> 3][i & 7] = (__bf16)p;
             sb[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dw[i]));
         }

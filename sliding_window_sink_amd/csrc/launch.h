@@ -54,7 +54,7 @@ struct BwdArgs {
     const void *q, *k, *v, *o, *dout;  // bf16, layouts as the prefill's
     const float *lse, *sink;           // forward lse [B,Hq,T] (natural log), sinks [Hq]
     float *dq, *dk, *dv, *dsink;       // fp32 outputs
-    float *D, *PS;                     // workspace, [B,Hq,T] each
+    float *D, *L2;                     // workspace, [B,Hq,T] each: D_i and lse_i * log2(e)
     int B, T, Hq, Hkv, window;
     float scale;
 };
