@@ -98,11 +98,41 @@ __device__ __forceinline__ void buf_store16_nt(BufRsrc r, uint32_t off, uint4 v)
 // acc / l); this only trades a bounded growth of p for fewer rescales.
 constexpr float kRescaleSlack = 8.0f;
 
-// Max over the two 32-lane halves of a wave (lanes l and l^32 hold the same column).
-__device__ __forceinline__ float max_across_halves(float x) {
-    return fmaxf(x, __shfl_xor(x, 32, 64));
+// Cross-lane exchanges on the VALU (gfx950's v_permlane32_swap / v_permlane16_swap)
+// instead of a ds_bpermute round trip through the LDS unit, which sat on the
+// softmax's critical path once per key block.  permlane32_swap(a, b) swaps rows
+// 2-3 of a with rows 0-1 of b (a row is 16 lanes); with a = b = x the two results
+// hold, in every lane l, x of lane l % 32 and of lane l % 32 + 32.
+// permlane16_swap(a, b) swaps the odd rows of a with the even rows of b: the
+// results hold x of rows (0, 1) in rows 0-1 and of rows (2, 3) in rows 2-3.
+__device__ __forceinline__ float2 lanes_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float sum_across_halves(float x) { return x + __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ float2 lanes_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Max / sum over the two 32-lane halves of a wave (lanes l and l^32 hold the same
+// column); the sum adds the lower half's value first in both lanes (the same bits
+// as x + x(l^32) in either lane: addition commutes).
+__device__ __forceinline__ float max_across_halves(float x) {
+    const float2 h = lanes_xor32(x);
+    return fmaxf(h.x, h.y);
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+    const float2 h = lanes_xor32(x);
+    return h.x + h.y;
+}
+// Over the four 16-lane rows (lanes l, l^16, l^32, l^48 hold the same column).
+__device__ __forceinline__ float max_across_rows(float x) {
+    const float2 h = lanes_xor16(x);
+    return max_across_halves(fmaxf(h.x, h.y));
+}
+__device__ __forceinline__ float sum_across_rows(float x) {
+    const float2 h = lanes_xor16(x);
+    return sum_across_halves(h.x + h.y);
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -345,8 +345,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             bm = fmaxf(bm, xs[e]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        bm = max_across_rows(bm);
         bm *= sl2;
         const bool up = bm > m + kRescaleSlack || (m == -INFINITY && bm > -INFINITY);
         const float mn = up ? bm : m;
@@ -417,8 +416,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     }
 
     // l is per lane group (16 lanes) -> total over the 4 groups of the column
-    float lt = l + __shfl_xor(l, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = sum_across_rows(l);
 
     // merge: the waves of phases 1 .. n_kh-1 of a column group park (acc, m, l) in
     // LDS (slot (phase-1) * n_cg + group); phase 0 folds them in, in phase order,

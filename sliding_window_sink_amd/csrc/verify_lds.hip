@@ -234,8 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_lds_kernel(CachedArgs a, f
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             bm = fmaxf(bm, xs[e]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-        bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+        bm = max_across_rows(bm);
         bm *= scale_log2;
         const bool up = bm > m + kRescaleSlack || (m == -INFINITY && bm > -INFINITY);
         const float mn = up ? bm : m;
@@ -323,8 +322,7 @@ __global__ __launch_bounds__(kThreads, 2) void verify_lds_kernel(CachedArgs a, f
     }
 
     // l is per lane group (16 lanes) -> total over the 4 groups of the column
-    float lt = l + __shfl_xor(l, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    const float lt = sum_across_rows(l);
     if (!col_ok)
         return;
     const bool write_final = a.n_splits == 1;
