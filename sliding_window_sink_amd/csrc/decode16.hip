@@ -85,7 +85,7 @@ __device__ __forceinline__ bf16x8 k_operand(const KV8 &x, int kt, int s) {
 __device__ __forceinline__ uint4 v_rows(const KV16 &x, int e) { return x.v[e]; }
 __device__ __forceinline__ uint4 v_rows(const KV8 &x, int e) { return e4m3x8_to_bf16x8(x.v[e]); }
 
-template <bool kTok, bool kFp8>
+template <bool kTok, bool kFp8, bool kSlots>
 __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, float scale_log2) {
     using KVc = typename std::conditional<kFp8, KV8, KV16>::type;  // cache block registers
     constexpr uint32_t kEs = kFp8 ? 1 : 2;  // bytes per cached element
@@ -107,6 +107,65 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     const int g = bg % Hkv, b = bg / Hkv;
     const int group = Hq / Hkv;
     const int n_cols = nq * group;
+    const size_t crow0 = ((size_t)b * Hkv + g) * a.cap;
+    const size_t nrow0 = (size_t)b * nq * Hkv + g;  // row of new token t: nrow0 + t*Hkv
+
+    // Q^T operand (B of the QK MFMA): column col = (token t, head) = divmod(col, group).
+    // Issued before the cache blocks, rotated once the RoPE table is ready (requested
+    // once the chunk is known to hold keys, or, in slot mode, at once).
+    const int n_cg = kTok ? min(kWaves, (n_cols + kCols - 1) / kCols) : 1;  // column groups
+    const int n_kh = kTok ? kWaves / n_cg : kWaves;  // key phases per column group
+    const int cw = kTok ? wave % n_cg : 0, kh = kTok ? wave / n_cg : wave;
+    const bool active = kh < n_kh;  // wave-uniform (3 column groups leave wave 3 idle)
+    const int col = kTok ? kCols * cw + lr : lr;
+    const bool col_ok = col < n_cols;
+    uint4 qr[kDqk / 32];
+    auto load_q = [&]() {
+        const BufRsrc qb = make_buf((const uint16_t *)a.q + (size_t)b * nq * Hq * kDqk,
+                                    (uint64_t)nq * Hq * kDqk * 2);
+        const uint32_t off =
+            col_ok ? (uint32_t)((col / group) * Hq + g * group + col % group) * kDqk * 2 : kOob;
+#pragma unroll
+        for (int s = 0; s < kDqk / 32; ++s)
+            qr[s] = buf_load16(qb, off + (uint32_t)kdim0<kFp8>(s, kg) * 2);
+    };
+    if constexpr (kSlots)
+        load_q();
+
+    // A one-token decode over a ring of exactly kWaves blocks (128 slots): wave w
+    // reads slots 32w .. 32w+31 in slot order, requested before the sequence
+    // length is known (every slot is in bounds).  Which position a slot holds,
+    // whether it is visible and which slot the new token replaces follow from the
+    // length once it arrives, so the cache loads do not wait for it.
+    // (kSlots: the launcher checked ring, nq == 1, cap == 128 and one split.)
+    constexpr bool slot_mode = kSlots;
+    static_assert(!kSlots || (!kTok && !kFp8), "slot order: one-token bf16 decode");
+    KVc x;
+    uint4 nk = make_uint4(0u, 0u, 0u, 0u), nv = nk;  // lane l: piece l of the new k / v row
+    if constexpr (kSlots) {
+        {
+            const BufRsrc kn0 = make_buf((const uint16_t *)a.k_new + nrow0 * kDqk, kDqk * 2);
+            const BufRsrc vn0 = make_buf((const uint16_t *)a.v_new + nrow0 * kDv, kDv * 2);
+            nk = buf_load16(kn0, lane < kDqk / 8 ? (uint32_t)lane * 16 : kOob);
+            nv = buf_load16(vn0, lane < kDv / 8 ? (uint32_t)lane * 16 : kOob);
+            const BufRsrc kc0 = make_buf((const uint8_t *)a.k_cache + crow0 * kDqk * kEs,
+                                         (uint64_t)a.cap * kDqk * kEs);
+            const BufRsrc vc0 = make_buf((const uint8_t *)a.v_cache + crow0 * kDv * kEs,
+                                         (uint64_t)a.cap * kDv * kEs);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const uint32_t off = (uint32_t)(kKb * wave + 16 * kt + lr) * kDqk * 2;
+#pragma unroll
+                for (int s = 0; s < kDqk / 32; ++s)
+                    x.k[kt][s] = buf_load16(kc0, off + (uint32_t)kdim0<false>(s, kg) * 2);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sl = kKb * wave + (e >> 2) * 16 + 4 * kg + (e & 3);
+                x.v[e] = buf_load16_nt(vc0, ((uint32_t)sl * kDv + (uint32_t)lr * 8) * 2);
+            }
+        }
+    }
     const int P = clamp_len(a.cache_len[b], a.max_len);
     const int lo = a.window > 0 ? max(0, P - a.window + 1) : 0;
     const int hi = P + nq;
@@ -115,9 +174,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
         rlo = max(lo, split * a.chunk);
         rhi = min(hi, (split + 1) * a.chunk);
     }
-
-    const size_t crow0 = ((size_t)b * Hkv + g) * a.cap;
-    const size_t nrow0 = (size_t)b * nq * Hkv + g;  // row of new token t: nrow0 + t*Hkv
 
     if (rlo >= rhi)
         return;  // uniform: this chunk holds no visible key
@@ -132,25 +188,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     const BufRsrc vn = make_buf((const uint16_t *)a.v_new + nrow0 * kDv,
                                 ((uint64_t)(nq - 1) * Hkv + 1) * kDv * 2);
 
-    // Q^T operand (B of the QK MFMA): column col = (token t, head) = divmod(col, group).
-    // Issued first, rotated once the RoPE table is ready.
-    const int n_cg = kTok ? min(kWaves, (n_cols + kCols - 1) / kCols) : 1;  // column groups
-    const int n_kh = kTok ? kWaves / n_cg : kWaves;  // key phases per column group
-    const int cw = kTok ? wave % n_cg : 0, kh = kTok ? wave / n_cg : wave;
-    const bool active = kh < n_kh;  // wave-uniform (3 column groups leave wave 3 idle)
-    const int col = kTok ? kCols * cw + lr : lr;
-    const bool col_ok = col < n_cols;
     const int qpos = col_ok ? P + col / group : -1;
-    uint4 qr[kDqk / 32];
-    {
-        const BufRsrc qb = make_buf((const uint16_t *)a.q + (size_t)b * nq * Hq * kDqk,
-                                    (uint64_t)nq * Hq * kDqk * 2);
-        const uint32_t off =
-            col_ok ? (uint32_t)((col / group) * Hq + g * group + col % group) * kDqk * 2 : kOob;
-#pragma unroll
-        for (int s = 0; s < kDqk / 32; ++s)
-            qr[s] = buf_load16(qb, off + (uint32_t)kdim0<kFp8>(s, kg) * 2);
-    }
+    if constexpr (!kSlots)
+        load_q();
     const int ce = min(rhi, P);
     const int n_cache_blk = ce > rlo ? (ce - rlo + kKb - 1) / kKb : 0;
     const int new_lo = max(rlo, P);
@@ -163,6 +203,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     const bool merge_new = !kTok && !kFp8 && nq == 1 && n_cache_blk > 0 && rhi > new_lo &&
                            P < rlo + n_cache_blk * kKb;
     const int nblk = n_cache_blk + (rhi > new_lo && !merge_new ? 1 : 0);
+    const int slot_new = P & (kWaves * kKb - 1);  // slot mode: the slot of position P
     const int window = a.window;
     const uint32_t krow = (uint32_t)Hkv * kDqk * 2, vrow = (uint32_t)Hkv * kDv * 2;
 
@@ -232,20 +273,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // The wave's first cache block is requested before the RoPE table and the
     // new-token store, so its memory latency overlaps that work (the store
     // writes position P, which no cache block reads).
-    const bool merge_wave = merge_new && (n_cache_blk - 1) % kWaves == wave;  // wave-uniform
-    uint4 nk = make_uint4(0u, 0u, 0u, 0u), nv = nk;  // lane l: piece l of the new k / v row
-    if (merge_wave) {
+    const bool merge_wave = slot_mode ? slot_new / kKb == wave
+                                      : merge_new && (n_cache_blk - 1) % kWaves == wave;  // wave-uniform
+    if (merge_wave && !slot_mode) {
         nk = buf_load16(kn, lane < kDqk / 8 ? (uint32_t)lane * 16 : kOob);
         nv = buf_load16(vn, lane < kDv / 8 ? (uint32_t)lane * 16 : kOob);
     }
-    KVc x;
     if constexpr (kTok) {
         if (active && kh < n_cache_blk) {
             load_k(kh, x);
             load_v(kh, x);
         }
     } else {
-        if (wave < n_cache_blk) {
+        if (!slot_mode && wave < n_cache_blk) {
             load_k(wave, x);
             load_v(wave, x);
         }
@@ -298,20 +338,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
         constexpr bool kCacheRegs = std::is_same<std::decay_t<decltype(x)>, KVc>::value;
         constexpr bool kScaled = kFp8 && kCacheRegs;  // E4M3 codes: fold the scales in
         const int kb = block_base(j);
-        const bool merged = kCacheRegs && merge_new && j == n_cache_blk - 1;
-        const int kend = j < n_cache_blk && !merged ? ce : rhi;
+        const bool merged = kCacheRegs && (slot_mode ? merge_wave : merge_new && j == n_cache_blk - 1);
+        const int kend = j < n_cache_blk && !merged && !slot_mode ? ce : rhi;
+        // position of key i of the block (slot mode: the slot's newest position <= P,
+        // negative for a slot not written yet) and whether it is the new token
+        auto key_pos = [&](int i) {
+            return slot_mode ? P - ((P - (kKb * wave + i)) & (kWaves * kKb - 1)) : kb + i;
+        };
         if constexpr (kCacheRegs && !kFp8) {
             if (merged) {  // lanes holding key P take its operands from the staged rows
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
-                    if (kb + 16 * kt + lr == P) {
+                    if (key_pos(16 * kt + lr) == P) {
 #pragma unroll
                         for (int s = 0; s < kDqk / 32; ++s)
                             x.k[kt][s] = new_row[kdim0<false>(s, kg) / 8];
                     }
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (kb + (e >> 2) * 16 + 4 * kg + (e & 3) == P)
+                    if (key_pos((e >> 2) * 16 + 4 * kg + (e & 3)) == P)
                         x.v[e] = new_row[kDqk / 8 + lr];
             }
         }
@@ -329,15 +374,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
                 load_k(jn, x);
         }
         // element e of this lane: key kb + (e/4)*16 + 4*kg + e%4, column lr
-        const bool full = j < n_cache_blk && !merged && kb + kKb <= ce && (window <= 0 || kb >= P + nq - window);
+        const bool full = slot_mode ? P >= kWaves * kKb - 1 && (window <= 0 || window >= kWaves * kKb)
+                                    : j < n_cache_blk && !merged && kb + kKb <= ce &&
+                                          (window <= 0 || kb >= P + nq - window);
         float xs[8];
+        uint32_t hidden = 0;  // slot mode: elements whose slot holds no position yet
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float v = sc[e >> 2][e & 3];
             if (!full) {
-                const int p = kb + (e >> 2) * 16 + 4 * kg + (e & 3);
-                const bool vis = p < kend && p <= qpos && (window <= 0 || qpos - p < window);
+                const int p = key_pos((e >> 2) * 16 + 4 * kg + (e & 3));
+                const bool vis = p >= 0 && p < kend && p <= qpos && (window <= 0 || qpos - p < window);
                 v = vis ? v : -INFINITY;
+                hidden |= p < 0 ? 1u << e : 0u;  // by key, whatever the lane's column
             }
             xs[e] = col_ok ? v : -INFINITY;
         }
@@ -372,6 +421,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             vr[e] = v_rows(x, e);
+        if (slot_mode && !full) {  // a slot not written yet may hold anything (NaN): zero it
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (hidden & (1u << e))
+                    vr[e] = make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             uint32_t w[4];
@@ -405,6 +460,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
                 compute(n_cache_blk, nblk, xn);
             }
         }
+    } else if (slot_mode) {
+        compute(wave, 1 << 30, x);  // the wave's 32 slots, the new token merged in
     } else {
         for (int j = wave; j < n_cache_blk; j += kWaves)
             compute(j, j + kWaves, x);
@@ -516,16 +573,19 @@ hipError_t launch_decode16(const CachedArgs &a, hipStream_t s) {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const dim3 grid((unsigned)(a.B * a.Hkv * a.n_splits)), block(kThreads);
     const bool tok = a.nq * (a.Hq / a.Hkv) > kCols;
+    const bool slots = a.ring && a.nq == 1 && a.cap == kWaves * kKb && a.n_splits == 1;
     if (a.fp8) {
         if (tok)
-            decode16_kernel<true, true><<<grid, block, 0, s>>>(a, scale_log2);
+            decode16_kernel<true, true, false><<<grid, block, 0, s>>>(a, scale_log2);
         else
-            decode16_kernel<false, true><<<grid, block, 0, s>>>(a, scale_log2);
+            decode16_kernel<false, true, false><<<grid, block, 0, s>>>(a, scale_log2);
     } else {
         if (tok)
-            decode16_kernel<true, false><<<grid, block, 0, s>>>(a, scale_log2);
+            decode16_kernel<true, false, false><<<grid, block, 0, s>>>(a, scale_log2);
+        else if (slots)
+            decode16_kernel<false, false, true><<<grid, block, 0, s>>>(a, scale_log2);
         else
-            decode16_kernel<false, false><<<grid, block, 0, s>>>(a, scale_log2);
+            decode16_kernel<false, false, false><<<grid, block, 0, s>>>(a, scale_log2);
     }
     return hipGetLastError();
 }
