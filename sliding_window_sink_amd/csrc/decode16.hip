@@ -378,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
                                     : j < n_cache_blk && !merged && kb + kKb <= ce &&
                                           (window <= 0 || kb >= P + nq - window);
         float xs[8];
-        uint32_t hidden = 0;  // slot mode: elements whose slot holds no position yet
+        uint32_t hidden = 0;  // slot mode: elements whose V rows must stay out of PV
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float v = sc[e >> 2][e & 3];
@@ -386,7 +386,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
                 const int p = key_pos((e >> 2) * 16 + 4 * kg + (e & 3));
                 const bool vis = p >= 0 && p < kend && p <= qpos && (window <= 0 || qpos - p < window);
                 v = vis ? v : -INFINITY;
-                hidden |= p < 0 ? 1u << e : 0u;  // by key, whatever the lane's column
+                // by key, whatever the lane's column: a slot not written yet, or one
+                // behind a window narrower than the ring (stale rows of any value)
+                hidden |= (p < 0 || (window > 0 && P - p >= window)) ? 1u << e : 0u;
             }
             xs[e] = col_ok ? v : -INFINITY;
         }

@@ -263,6 +263,22 @@ def test_decode_ring(dtype, Hq, Hkv):
         assert torch.equal(vc[b, :, L % 128], layer.v_new[b, 0])
 
 
+@pytest.mark.parametrize("window", [100, 1])
+def test_decode_ring_window_below_capacity(window):
+    """A 128-slot ring under a narrower window: the one-token kernel reads every
+    slot, so the slots behind the window (stale rows; here the oldest history row
+    and NaN-poisoned slots never written) must stay out of the output."""
+    _print_case("decode ring window below capacity", window)
+    lens = [0, 1, window - 1, window, window + 1, 127, 128, 129, 1000]
+    cl = torch.tensor(lens, dtype=torch.int32)
+    layer = _layer(27 + window, cl, 1, 64, 8, window)
+    o, kc, vc = _run_cached(layer, cl, ops.RING, window, 128, 8, verify=False)
+    assert_close(o, _ref_cached(layer, cl, window), torch.bfloat16, "ring decode W < cap")
+    kc = kc.cpu()
+    for b, L in enumerate(lens):
+        assert torch.equal(kc[b, :, L % 128], layer.k_new[b, 0])
+
+
 def test_decode_ring_wide_window():
     """W = 512 (the width of the report's window-size ablation, Table 2) as a runtime
     parameter of the ring decode: up to 512 visible keys (the query included) over
