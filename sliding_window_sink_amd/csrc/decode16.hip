@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // key block (phase w / n_cg); the phases of a group merge like the waves of
     // the other mode (the waves stream the same rows: one HBM read, L2 hits).
     constexpr int kMerge = kWaves - 1;  // parked states at most
-    __shared__ __attribute__((aligned(16))) float merge[kMerge][kCols][kMergeStride];
+    __shared__ __attribute__((aligned(16))) float merge[kTok ? kMerge : kWaves][kCols][kMergeStride];
     __shared__ float2 rope_tab[(kTok ? kMaxNqTok : kMaxNq) * 32];
     __shared__ uint4 new_row[(kDqk + kDv) / 8];  // one new token's k, v rows (merged block)
     const int tid = threadIdx.x, lane = tid & 63;
@@ -477,94 +477,185 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // l is per lane group (16 lanes) -> total over the 4 groups of the column
     const float lt = sum_across_rows(l);
 
-    // merge: the waves of phases 1 .. n_kh-1 of a column group park (acc, m, l) in
-    // LDS (slot (phase-1) * n_cg + group); phase 0 folds them in, in phase order,
-    // and writes.  acc[db][i] holds dim 8*(4kg + i) + db of column lr.
-    const int n_park = n_kh - 1;
-    if (active && kh > 0 && col_ok) {
-        float *e = &merge[(kh - 1) * n_cg + cw][lr][0];
-        if (kg == 0) {
-            e[kDv] = m;
-            e[kDv + 1] = lt;
-        }
+    if constexpr (!kTok) {
+        // merge: every wave parks (acc, m, l) in LDS slot `wave`; after one barrier
+        // wave w finalizes dims 8*(4kg + w) .. +7 of each column (lane (lr, kg)) from
+        // the four slots in wave order, so the merge and the output stores are
+        // spread over the four waves.  acc[db][i] holds dim 8*(4kg + i) + db of
+        // column lr.
+        if (col_ok) {
+            float *e = &merge[wave][lr][0];
+            if (kg == 0) {
+                e[kDv] = m;
+                e[kDv + 1] = lt;
+            }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d0 = 8 * (4 * kg + i);
-            *(float4 *)&e[d0] = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
-            *(float4 *)&e[d0 + 4] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 8 * (4 * kg + i);
+                *(float4 *)&e[d0] = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+                *(float4 *)&e[d0 + 4] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+            }
         }
-    }
-    if (n_park > 0)  // uniform
         __syncthreads();
-    if (active && kh == 0 && col_ok) {
+        if (!col_ok)
+            return;
         const bool write_final = a.n_splits == 1;
         const size_t rows_total = (size_t)a.B * nq * Hq;
-        const int t = col / group;
         const int h = g * group + col % group;
-        const size_t row = ((size_t)b * nq + t) * Hq + h;
-        float mx = m;
+        const size_t row = ((size_t)b * nq + col / group) * Hq + h;
+        float mw[kWaves], fw[kWaves];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kMerge; ++w)
-            if (w < n_park)
-                mx = fmaxf(mx, merge[w * n_cg + cw][lr][kDv]);
-        float M = mx, zs = 0.f;
+        for (int w = 0; w < kWaves; ++w) {
+            mw[w] = merge[w][lr][kDv];
+            mx = fmaxf(mx, mw[w]);
+        }
+        float M = mx, z = 0.f;
         if (write_final) {
             const float sink2 = a.sink[h] * kLog2e;
             M = fmaxf(mx, sink2);
-            zs = (sink2 == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(sink2 - M);
+            z = (sink2 == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(sink2 - M);
         }
-        const float f0 = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
-        float fw[kMerge];
-        float z = zs + lt * f0;
 #pragma unroll
-        for (int w = 0; w < kMerge; ++w) {
-            fw[w] = 0.f;
-            if (w < n_park) {
-                const float mw = merge[w * n_cg + cw][lr][kDv];
-                fw[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-                z += merge[w * n_cg + cw][lr][kDv + 1] * fw[w];
-            }
+        for (int w = 0; w < kWaves; ++w) {
+            fw[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);
+            z += merge[w][lr][kDv + 1] * fw[w];
         }
         const float so = write_final ? (z > 0.f ? 1.f / z : 0.f) : 1.f;
+        const int d0 = 8 * (4 * kg + wave);
+        float vals[8];
+        {
+            const float4 p0 = *(const float4 *)&merge[0][lr][d0];
+            const float4 p1 = *(const float4 *)&merge[0][lr][d0 + 4];
+            vals[0] = p0.x * fw[0];
+            vals[1] = p0.y * fw[0];
+            vals[2] = p0.z * fw[0];
+            vals[3] = p0.w * fw[0];
+            vals[4] = p1.x * fw[0];
+            vals[5] = p1.y * fw[0];
+            vals[6] = p1.z * fw[0];
+            vals[7] = p1.w * fw[0];
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d0 = 8 * (4 * kg + i);
-            float vals[8];
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-                vals[db] = acc[db][i] * f0;
-#pragma unroll
-            for (int w = 0; w < kMerge; ++w) {
-                if (w >= n_park)
-                    break;
-                const float4 p0 = *(const float4 *)&merge[w * n_cg + cw][lr][d0];
-                const float4 p1 = *(const float4 *)&merge[w * n_cg + cw][lr][d0 + 4];
-                vals[0] += p0.x * fw[w];
-                vals[1] += p0.y * fw[w];
-                vals[2] += p0.z * fw[w];
-                vals[3] += p0.w * fw[w];
-                vals[4] += p1.x * fw[w];
-                vals[5] += p1.y * fw[w];
-                vals[6] += p1.z * fw[w];
-                vals[7] += p1.w * fw[w];
-            }
-            if (write_final) {
-                uint4 u;
-                u.x = pack_bf16x2(vals[0] * so, vals[1] * so);
-                u.y = pack_bf16x2(vals[2] * so, vals[3] * so);
-                u.z = pack_bf16x2(vals[4] * so, vals[5] * so);
-                u.w = pack_bf16x2(vals[6] * so, vals[7] * so);
-                *(uint4 *)((uint16_t *)a.o + row * kDv + d0) = u;
-            } else {
-                float *dst = &a.ws[2 * rows_total * a.n_splits + (row * a.n_splits + split) * kDv + d0];
-                *(float4 *)dst = make_float4(vals[0], vals[1], vals[2], vals[3]);
-                *(float4 *)(dst + 4) = make_float4(vals[4], vals[5], vals[6], vals[7]);
+        for (int w = 1; w < kWaves; ++w) {
+            const float4 p0 = *(const float4 *)&merge[w][lr][d0];
+            const float4 p1 = *(const float4 *)&merge[w][lr][d0 + 4];
+            vals[0] += p0.x * fw[w];
+            vals[1] += p0.y * fw[w];
+            vals[2] += p0.z * fw[w];
+            vals[3] += p0.w * fw[w];
+            vals[4] += p1.x * fw[w];
+            vals[5] += p1.y * fw[w];
+            vals[6] += p1.z * fw[w];
+            vals[7] += p1.w * fw[w];
+        }
+        if (write_final) {
+            uint4 u;
+            u.x = pack_bf16x2(vals[0] * so, vals[1] * so);
+            u.y = pack_bf16x2(vals[2] * so, vals[3] * so);
+            u.z = pack_bf16x2(vals[4] * so, vals[5] * so);
+            u.w = pack_bf16x2(vals[6] * so, vals[7] * so);
+            *(uint4 *)((uint16_t *)a.o + row * kDv + d0) = u;
+        } else {
+            float *dst = &a.ws[2 * rows_total * a.n_splits + (row * a.n_splits + split) * kDv + d0];
+            *(float4 *)dst = make_float4(vals[0], vals[1], vals[2], vals[3]);
+            *(float4 *)(dst + 4) = make_float4(vals[4], vals[5], vals[6], vals[7]);
+            if (kg == 0 && wave == 0) {
+                const size_t slot = row * a.n_splits + split;
+                a.ws[slot] = M;
+                a.ws[rows_total * a.n_splits + slot] = (M == -INFINITY) ? 0.f : z;
             }
         }
-        if (!write_final && kg == 0) {
-            const size_t slot = row * a.n_splits + split;
-            a.ws[slot] = M;
-            a.ws[rows_total * a.n_splits + slot] = (M == -INFINITY) ? 0.f : z;
+    } else {
+        // merge: the waves of phases 1 .. n_kh-1 of a column group park (acc, m, l) in
+        // LDS (slot (phase-1) * n_cg + group); phase 0 folds them in, in phase order,
+        // and writes.  acc[db][i] holds dim 8*(4kg + i) + db of column lr.
+        const int n_park = n_kh - 1;
+        if (active && kh > 0 && col_ok) {
+            float *e = &merge[(kh - 1) * n_cg + cw][lr][0];
+            if (kg == 0) {
+                e[kDv] = m;
+                e[kDv + 1] = lt;
+            }
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 8 * (4 * kg + i);
+                *(float4 *)&e[d0] = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+                *(float4 *)&e[d0 + 4] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+            }
+        }
+        if (n_park > 0)  // uniform
+            __syncthreads();
+        if (active && kh == 0 && col_ok) {
+            const bool write_final = a.n_splits == 1;
+            const size_t rows_total = (size_t)a.B * nq * Hq;
+            const int t = col / group;
+            const int h = g * group + col % group;
+            const size_t row = ((size_t)b * nq + t) * Hq + h;
+            float mx = m;
+    #pragma unroll
+            for (int w = 0; w < kMerge; ++w)
+                if (w < n_park)
+                    mx = fmaxf(mx, merge[w * n_cg + cw][lr][kDv]);
+            float M = mx, zs = 0.f;
+            if (write_final) {
+                const float sink2 = a.sink[h] * kLog2e;
+                M = fmaxf(mx, sink2);
+                zs = (sink2 == -INFINITY || M == -INFINITY) ? 0.f : fast_exp2(sink2 - M);
+            }
+            const float f0 = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+            float fw[kMerge];
+            float z = zs + lt * f0;
+    #pragma unroll
+            for (int w = 0; w < kMerge; ++w) {
+                fw[w] = 0.f;
+                if (w < n_park) {
+                    const float mw = merge[w * n_cg + cw][lr][kDv];
+                    fw[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+                    z += merge[w * n_cg + cw][lr][kDv + 1] * fw[w];
+                }
+            }
+            const float so = write_final ? (z > 0.f ? 1.f / z : 0.f) : 1.f;
+    #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 8 * (4 * kg + i);
+                float vals[8];
+    #pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    vals[db] = acc[db][i] * f0;
+    #pragma unroll
+                for (int w = 0; w < kMerge; ++w) {
+                    if (w >= n_park)
+                        break;
+                    const float4 p0 = *(const float4 *)&merge[w * n_cg + cw][lr][d0];
+                    const float4 p1 = *(const float4 *)&merge[w * n_cg + cw][lr][d0 + 4];
+                    vals[0] += p0.x * fw[w];
+                    vals[1] += p0.y * fw[w];
+                    vals[2] += p0.z * fw[w];
+                    vals[3] += p0.w * fw[w];
+                    vals[4] += p1.x * fw[w];
+                    vals[5] += p1.y * fw[w];
+                    vals[6] += p1.z * fw[w];
+                    vals[7] += p1.w * fw[w];
+                }
+                if (write_final) {
+                    uint4 u;
+                    u.x = pack_bf16x2(vals[0] * so, vals[1] * so);
+                    u.y = pack_bf16x2(vals[2] * so, vals[3] * so);
+                    u.z = pack_bf16x2(vals[4] * so, vals[5] * so);
+                    u.w = pack_bf16x2(vals[6] * so, vals[7] * so);
+                    *(uint4 *)((uint16_t *)a.o + row * kDv + d0) = u;
+                } else {
+                    float *dst = &a.ws[2 * rows_total * a.n_splits + (row * a.n_splits + split) * kDv + d0];
+                    *(float4 *)dst = make_float4(vals[0], vals[1], vals[2], vals[3]);
+                    *(float4 *)(dst + 4) = make_float4(vals[4], vals[5], vals[6], vals[7]);
+                }
+            }
+            if (!write_final && kg == 0) {
+                const size_t slot = row * a.n_splits + split;
+                a.ws[slot] = M;
+                a.ws[rows_total * a.n_splits + slot] = (M == -INFINITY) ? 0.f : z;
+            }
         }
     }
 }
