@@ -285,12 +285,13 @@ __device__ __forceinline__ uint2 bf16x8_to_e4m3x8(uint4 x, float scale) {
 // k rotated when kRope); with kRope a k_rot output receives every new token's
 // rotated k.  tab holds the (cos, sin) of positions P .. P+nq-1 when kRope.  Nothing in
 // the launch reads the rows written here.
+// store_cache = false leaves the cache store to the caller (which holds the rows).
 template <bool kRope, bool kFp8 = false>
 __device__ __forceinline__ void cached_store_new(const CachedArgs &a, size_t crow0, size_t nrow0,
                                                  int P, const float2 *tab, int tid,
-                                                 int nthreads) {
+                                                 int nthreads, bool store_cache = true) {
     const uint16_t *ks = (const uint16_t *)a.k_new;
-    if (a.write_new && (a.ring || P < a.cap)) {
+    if (store_cache && a.write_new && (a.ring || P < a.cap)) {
         const int slot = a.ring ? (P % a.cap) : P;
         const uint16_t *vs = (const uint16_t *)a.v_new + nrow0 * kDv;
         for (int i = tid; i < (kDqk + kDv) / 8; i += nthreads) {

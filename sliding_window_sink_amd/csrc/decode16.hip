@@ -299,20 +299,29 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     // The chunk holding position P stores the new token (decode) / rotated keys.
     if (P >= rlo && P < rhi) {
         if (a.rope)
-            cached_store_new<true, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
+            cached_store_new<true, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads, !kSlots);
         else
-            cached_store_new<false, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads);
+            cached_store_new<false, kFp8>(a, crow0, nrow0, P, rope_tab, tid, kThreads, !kSlots);
     }
 
     if (merge_wave) {  // wave-private: the same wave reads the rows back (LDS keeps its order)
+        // slot mode: this wave also stores the token into the cache from these
+        // registers (slot P mod 128), instead of the workgroup reading k_new / v_new
+        // again for the store
+        const bool store = kSlots && a.write_new;
         if (lane < kDqk / 8) {
             uint4 v = nk;
             if (a.rope && lane < 8)
                 v = rope_chunk_bf16(v, rope_tab + 4 * lane);
             new_row[lane] = v;
+            if (store)
+                *(uint4 *)((uint16_t *)a.k_cache + (crow0 + slot_new) * kDqk + lane * 8) = v;
         }
-        if (lane < kDv / 8)
+        if (lane < kDv / 8) {
             new_row[kDqk / 8 + lane] = nv;
+            if (store)
+                *(uint4 *)((uint16_t *)a.v_cache + (crow0 + slot_new) * kDv + lane * 8) = nv;
+        }
     }
 
     bf16x8 qf[kDqk / 32];
