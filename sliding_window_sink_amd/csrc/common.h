@@ -213,6 +213,15 @@ __device__ __forceinline__ void rope_fill_table64(float2 *tab, int pos0, int n, 
     for (int i = tid; i < n * 32; i += nthreads)
         tab[i] = rope_cos_sin(pos0 + (i >> 5), rope_inv_freq(base, i & 31, 64));
 }
+// The same table from a frequency the thread computed beforehand, inv_freq =
+// rope_inv_freq(base, tid % 32, 64) (nthreads a multiple of 32, so every entry the
+// thread fills has pair tid % 32): the fp64 pow can then run before the position
+// is known.
+__device__ __forceinline__ void rope_fill_table64_inv(float2 *tab, int pos0, int n, double inv_freq,
+                                                      int tid, int nthreads) {
+    for (int i = tid; i < n * 32; i += nthreads)
+        tab[i] = rope_cos_sin(pos0 + (i >> 5), inv_freq);
+}
 // Rotate the 4 interleaved pairs held in 8 bf16 (one 16-byte chunk); cs[p] is the
 // (cos, sin) of pair p of the chunk.
 __device__ __forceinline__ uint4 rope_chunk_bf16(uint4 x, const float2 *cs) {

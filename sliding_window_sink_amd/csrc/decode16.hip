@@ -142,7 +142,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     static_assert(!kSlots || (!kTok && !kFp8), "slot order: one-token bf16 decode");
     KVc x;
     uint4 nk = make_uint4(0u, 0u, 0u, 0u), nv = nk;  // lane l: piece l of the new k / v row
+    // Slot mode reads the length through a vector load issued ahead of the cache
+    // blocks (a scalar load would be waited for together with the kernel's other
+    // scalar loads), so the fp64 RoPE frequency below runs while it is on its way.
+    uint32_t len_v = 0;
     if constexpr (kSlots) {
+        len_v = __builtin_amdgcn_raw_buffer_load_b32(make_buf(a.cache_len + b, 4), 0u, 0, 0);
         {
             const BufRsrc kn0 = make_buf((const uint16_t *)a.k_new + nrow0 * kDqk, kDqk * 2);
             const BufRsrc vn0 = make_buf((const uint16_t *)a.v_new + nrow0 * kDv, kDv * 2);
@@ -166,7 +171,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
             }
         }
     }
-    const int P = clamp_len(a.cache_len[b], a.max_len);
+    const double inv_freq = kSlots && a.rope ? rope_inv_freq(a.rope_base, tid & 31, 64) : 0.0;
+    const int P = clamp_len(kSlots ? (int)__builtin_amdgcn_readfirstlane(len_v) : a.cache_len[b],
+                            a.max_len);
     const int lo = a.window > 0 ? max(0, P - a.window + 1) : 0;
     const int hi = P + nq;
     int rlo = lo, rhi = hi;
@@ -293,7 +300,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
 
     // RoPE (when fused): (cos, sin) of positions P .. P+nq-1 for q and the new keys.
     if (a.rope) {
-        rope_fill_table64(rope_tab, P, nq, a.rope_base, tid, kThreads);
+        if constexpr (kSlots)
+            rope_fill_table64_inv(rope_tab, P, nq, inv_freq, tid, kThreads);
+        else
+            rope_fill_table64(rope_tab, P, nq, a.rope_base, tid, kThreads);
         __syncthreads();
     }
     // The chunk holding position P stores the new token (decode) / rotated keys.
