@@ -29,6 +29,10 @@
 // the new token into the cache in the same launch (the attention reads
 // positions >= P from k_new).  Chunks that hold no key return at once: the
 // combine only reads the chunks that intersect the visible range.
+// A one-token decode over a 128-slot ring (kSlots) reads the ring in slot order,
+// one 32-slot block per wave, before the sequence length arrives; the length then
+// tells each slot's position, which slots are visible, and which slot the new
+// token replaces (that wave computes and stores it from registers).
 #include <type_traits>
 
 #include "common.h"
