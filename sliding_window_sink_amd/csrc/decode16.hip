@@ -152,27 +152,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode16_kernel(CachedArgs a, flo
     uint32_t len_v = 0;
     if constexpr (kSlots) {
         len_v = __builtin_amdgcn_raw_buffer_load_b32(make_buf(a.cache_len + b, 4), 0u, 0, 0);
-        {
-            const BufRsrc kn0 = make_buf((const uint16_t *)a.k_new + nrow0 * kDqk, kDqk * 2);
-            const BufRsrc vn0 = make_buf((const uint16_t *)a.v_new + nrow0 * kDv, kDv * 2);
-            nk = buf_load16(kn0, lane < kDqk / 8 ? (uint32_t)lane * 16 : kOob);
-            nv = buf_load16(vn0, lane < kDv / 8 ? (uint32_t)lane * 16 : kOob);
-            const BufRsrc kc0 = make_buf((const uint8_t *)a.k_cache + crow0 * kDqk * kEs,
-                                         (uint64_t)a.cap * kDqk * kEs);
-            const BufRsrc vc0 = make_buf((const uint8_t *)a.v_cache + crow0 * kDv * kEs,
-                                         (uint64_t)a.cap * kDv * kEs);
+        const BufRsrc kn0 = make_buf((const uint16_t *)a.k_new + nrow0 * kDqk, kDqk * 2);
+        const BufRsrc vn0 = make_buf((const uint16_t *)a.v_new + nrow0 * kDv, kDv * 2);
+        nk = buf_load16(kn0, lane < kDqk / 8 ? (uint32_t)lane * 16 : kOob);
+        nv = buf_load16(vn0, lane < kDv / 8 ? (uint32_t)lane * 16 : kOob);
+        const BufRsrc kc0 = make_buf((const uint8_t *)a.k_cache + crow0 * kDqk * kEs,
+                                     (uint64_t)a.cap * kDqk * kEs);
+        const BufRsrc vc0 = make_buf((const uint8_t *)a.v_cache + crow0 * kDv * kEs,
+                                     (uint64_t)a.cap * kDv * kEs);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const uint32_t off = (uint32_t)(kKb * wave + 16 * kt + lr) * kDqk * 2;
+        for (int kt = 0; kt < 2; ++kt) {
+            const uint32_t off = (uint32_t)(kKb * wave + 16 * kt + lr) * kDqk * 2;
 #pragma unroll
-                for (int s = 0; s < kDqk / 32; ++s)
-                    x.k[kt][s] = buf_load16(kc0, off + (uint32_t)kdim0<false>(s, kg) * 2);
-            }
+            for (int s = 0; s < kDqk / 32; ++s)
+                x.k[kt][s] = buf_load16(kc0, off + (uint32_t)kdim0<false>(s, kg) * 2);
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sl = kKb * wave + (e >> 2) * 16 + 4 * kg + (e & 3);
-                x.v[e] = buf_load16_nt(vc0, ((uint32_t)sl * kDv + (uint32_t)lr * 8) * 2);
-            }
+        for (int e = 0; e < 8; ++e) {
+            const int sl = kKb * wave + (e >> 2) * 16 + 4 * kg + (e & 3);
+            x.v[e] = buf_load16_nt(vc0, ((uint32_t)sl * kDv + (uint32_t)lr * 8) * 2);
         }
     }
     const double inv_freq = kSlots && a.rope ? rope_inv_freq(a.rope_base, tid & 31, 64) : 0.0;
